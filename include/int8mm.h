@@ -1,0 +1,151 @@
+/*
+ * int8mm.h - C ABI of libint8mm.so: the LLM.int8() mixed-precision
+ * decomposed matrix multiply on MI355X (gfx950).
+ *
+ * Sources (web pages on the method, cited by title and section):
+ *   [Abstract]  "LLM.int8(): 8-bit Matrix Multiplication for Transformers at
+ *               Scale" (mlsanity.com paper index), "Abstract (arXiv)".
+ *   [Summary]   "8-bit Matrix Multiplication for Large Language Models"
+ *               (legiblepapers.com), "Summary & Methodology Analysis".
+ *   [Blog]      "Compress your LLMs" (samsena.com), bullets "Vector-wise
+ *               quantization" and "Mixed-precision decomposition".
+ *   [Explainer] "What is 8-bit LLM quantization?" (machinoai.in), "How does
+ *               INT8 quantization work?".
+ *
+ * Notation: X fp16 [M, K] row-major activations (rows = tokens, columns =
+ * feature dimensions). W fp16 weights, K input features x N output features.
+ * Wq int8 [N, K] row-major (K contiguous). Codes are symmetric in
+ * [-127, 127]: q = round-half-even(127 * v / a) for absmax constant a, and
+ * q = 0 when a = 0. An outlier column j is one where some row has
+ * |X[i, j]| >= threshold.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *    owned by the caller. The library never allocates device memory, never
+ *    frees, and keeps no pointer after returning. Inputs are never written;
+ *    outputs are fully overwritten. Buffers must not overlap.
+ *  - Every pointer must be 16-byte aligned. K and N must be multiples of 16
+ *    (>= 16). 1 <= M, N <= 2^24. K <= 133144, which keeps |int32 accumulators|
+ *    <= 127*127*K < 2^31. 0 <= max_outliers <= min(K, 8192).
+ *  - Calls are stream-ordered and asynchronous on `stream` (0 = the null
+ *    stream). They make no host synchronisation and read no device data on
+ *    the host (int8mm_read_status and int8mm_timing_read excepted).
+ *  - Argument errors are found on the host before any HIP call and returned
+ *    synchronously (nothing is launched). A failed launch returns
+ *    INT8MM_E_HIP. Inputs must be finite.
+ */
+#ifndef INT8MM_H_
+#define INT8MM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum int8mm_status {
+  INT8MM_OK = 0,
+  INT8MM_E_NULL = 1,      /* a required pointer is NULL */
+  INT8MM_E_SHAPE = 2,     /* M, K, N or max_outliers outside the limits above,
+                             or a bad layout flag */
+  INT8MM_E_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  INT8MM_E_THRESHOLD = 4, /* threshold is NaN or negative */
+  INT8MM_E_WORKSPACE = 5, /* workspace smaller than int8_mixed_matmul_workspace_bytes() */
+  INT8MM_E_HIP = 6,       /* a HIP runtime call or kernel launch failed */
+  INT8MM_E_TOO_MANY_OUTLIERS = 7 /* asynchronous: more outlier columns than max_outliers;
+                                    reported only through int8mm_read_status */
+} int8mm_status;
+
+/*
+ * Weight conversion, once per weight ([Abstract]: a 16/32-bit checkpoint is
+ * converted to Int8 at load; [Blog] "Vector-wise quantization": one constant
+ * per column of the weight matrix).
+ *   W         fp16 weights. w_layout 0: [K, N] row-major (x @ W);
+ *             w_layout 1: [N, K] row-major (the nn.Linear weight layout).
+ *   Wq        out, int8 [N, K] row-major: Wq[n, k] = q(W(k, n), w_absmax[n]).
+ *   w_absmax  out, fp32 [N]: max over all K of |W(k, n)| (an exact fp16 value).
+ */
+int int8_prepare_weight(const void* W, int64_t K, int64_t N, int w_layout, int8_t* Wq,
+                        float* w_absmax, hipStream_t stream);
+
+/*
+ * Outlier detection plus vector-wise row quantization of the activations
+ * ([Blog] "Vector-wise quantization": one constant per input row;
+ * [Abstract]/[Summary]: outlier feature dimensions are isolated).
+ *   X             fp16 [M, K] row-major.
+ *   threshold     >= 0. +inf: no outliers. 0: every column is an outlier.
+ *   Xq            out, int8 [M, K]: 0 in outlier columns, else q(X[i,j], x_absmax[i]).
+ *   x_absmax      out, fp32 [M]: max |X[i, j]| over non-outlier columns j (0 if none).
+ *   outlier_mask  out, uint32 [ceil(K/32)]: bit (j % 32) of word j / 32 set iff
+ *                 column j is an outlier.
+ *   outlier_idx   out, int32 [max_outliers] (may be NULL when max_outliers == 0):
+ *                 the first min(count, max_outliers) outlier columns, ascending.
+ *   n_outliers    out, int32 [1]: the true outlier count (may exceed max_outliers).
+ */
+int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t* Xq,
+                    float* x_absmax, uint32_t* outlier_mask, int32_t* outlier_idx,
+                    int32_t* n_outliers, int64_t max_outliers, hipStream_t stream);
+
+/* Bytes of workspace int8_mixed_matmul needs for this shape (0 on bad arguments). */
+size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers);
+
+/*
+ * The decomposed product Y = dequant(Xq Wq^T) + X[:, O] W^[O, :] in fp16
+ * ([Summary]: the int8 product is dequantized by the outer product of the
+ * row and column constants, and the outlier and regular outputs are summed
+ * into 16-bit floating-point outputs; [Blog] "Mixed-precision
+ * decomposition": outlier dimensions in 16 bit, the rest in 8 bit).
+ *   X, M, K       fp16 activations [M, K].
+ *   Wq, w_absmax  int8 [N, K] and fp32 [N] from int8_prepare_weight.
+ *   threshold     outlier threshold, as for int8_quant_rows.
+ *   max_outliers  capacity for outlier columns, 0 <= max_outliers <= min(K, 8192). If the
+ *                 call finds more, Y is filled with fp16 NaN and the workspace
+ *                 status becomes INT8MM_E_TOO_MANY_OUTLIERS.
+ *   Y             out, fp16 [M, N] row-major.
+ *   workspace     device scratch of at least workspace_bytes; contents on entry
+ *                 are ignored. It also holds the status word of the last call.
+ *   acc_i32       optional out (NULL to skip), int32 [M, N]: the exact int8
+ *                 accumulators sum_k Xq[i,k] Wq[n,k], for verification.
+ * Sums: int32 exact for the int8 part; the outlier part uses fp16 operands
+ * (X values and Wq*w_absmax/127 rounded to fp16) with fp32 accumulation; the
+ * epilogue combines both in fp32 and rounds once to fp16.
+ * M <= 16, K <= 8192 and M*K <= 32768 run as one bandwidth-bound kernel; otherwise three
+ * kernels (outlier mask, row quantization + outlier gathers, MFMA GEMM).
+ */
+int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                      const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
+                      void* Y, void* workspace, size_t workspace_bytes, int32_t* acc_i32,
+                      hipStream_t stream);
+
+/* 1 if int8_mixed_matmul takes the single-kernel decode path for (M, K), else 0. */
+int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
+
+/*
+ * Synchronises `stream`, then returns the status word the last
+ * int8_mixed_matmul call left in `workspace` (INT8MM_OK or
+ * INT8MM_E_TOO_MANY_OUTLIERS), or INT8MM_E_HIP / INT8MM_E_NULL.
+ * n_outliers (nullable) receives that call's outlier count.
+ */
+int int8mm_read_status(const void* workspace, int32_t* n_outliers, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* int8mm_strerror(int code);
+
+/*
+ * Optional timing of the main kernel (the MFMA GEMM, or the decode kernel):
+ * while enabled, each int8_mixed_matmul call records a HIP event pair around
+ * that launch on its stream. int8mm_timing_read synchronises on the recorded
+ * events, returns the summed milliseconds and launch count since the last
+ * read, and starts a new period. Not thread-safe.
+ */
+int int8mm_timing_enable(int enable);
+int int8mm_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8MM_H_ */

@@ -1,0 +1,183 @@
+"""ctypes binding of libint8mm.so (declared in include/int8mm.h).
+
+Argument marshalling only: torch allocates device memory and supplies the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels. There is no CPU fallback: if the library is missing or fails to load,
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8mm.so")
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_f32 = ctypes.c_float
+
+# name -> (restype, argtypes); exactly the symbols include/int8mm.h declares
+SIGNATURES = {
+    "int8_prepare_weight": (_int, [_p, _i64, _i64, _int, _p, _p, _p]),
+    "int8_quant_rows": (_int, [_p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _i64, _p]),
+    "int8_mixed_matmul_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "int8_mixed_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _f32, _i64, _p, _p,
+                                 ctypes.c_size_t, _p, _p]),
+    "int8_mixed_matmul_is_decode": (_int, [_i64, _i64]),
+    "int8mm_read_status": (_int, [_p, _p, _p]),
+    "int8mm_strerror": (ctypes.c_char_p, [_int]),
+    "int8mm_timing_enable": (_int, [_int]),
+    "int8mm_timing_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+}
+
+STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_ALIGN", 4: "E_THRESHOLD",
+          5: "E_WORKSPACE", 6: "E_HIP", 7: "E_TOO_MANY_OUTLIERS"}
+
+_lib = None
+
+
+class Int8mmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: int8mm status {code} ({STATUS.get(code, '?')}): "
+                         f"{strerror(code)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libint8mm.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(python -m int8_mixed_precision_col_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().int8mm_strerror(code).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise Int8mmError(rc, where)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a HIP device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prepare_weight(W: torch.Tensor, layout: int = 0):
+    """fp16 W ([K, N] for layout 0, [N, K] for layout 1) -> (Wq int8 [N, K], a_w fp32 [N])."""
+    _need(W, torch.float16, "W")
+    K, N = (W.shape[0], W.shape[1]) if layout == 0 else (W.shape[1], W.shape[0])
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    a_w = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib().int8_prepare_weight(W.data_ptr(), K, N, layout, Wq.data_ptr(), a_w.data_ptr(),
+                                     _stream(W)), "int8_prepare_weight")
+    return Wq, a_w
+
+
+def quant_rows(X: torch.Tensor, threshold: float, max_outliers: int = 256) -> dict:
+    """Outlier columns + row quantization of fp16 X [M, K] (see include/int8mm.h)."""
+    _need(X, torch.float16, "X")
+    M, K = X.shape
+    dev = X.device
+    out = {
+        "Xq": torch.empty((M, K), dtype=torch.int8, device=dev),
+        "a_x": torch.empty((M,), dtype=torch.float32, device=dev),
+        "mask": torch.empty(((K + 31) // 32,), dtype=torch.int32, device=dev),
+        "idx": torch.empty((max(max_outliers, 1),), dtype=torch.int32, device=dev),
+        "count": torch.empty((4,), dtype=torch.int32, device=dev),
+    }
+    _check(lib().int8_quant_rows(X.data_ptr(), M, K, float(threshold), out["Xq"].data_ptr(),
+                                 out["a_x"].data_ptr(), out["mask"].data_ptr(),
+                                 out["idx"].data_ptr() if max_outliers > 0 else None,
+                                 out["count"].data_ptr(), max_outliers, _stream(X)),
+           "int8_quant_rows")
+    return out
+
+
+def workspace_bytes(M: int, K: int, N: int, max_outliers: int = 256) -> int:
+    return int(lib().int8_mixed_matmul_workspace_bytes(M, K, N, max_outliers))
+
+
+def is_decode(M: int, K: int) -> bool:
+    return bool(lib().int8_mixed_matmul_is_decode(M, K))
+
+
+def make_workspace(M: int, K: int, N: int, max_outliers: int = 256, device="cuda") -> torch.Tensor:
+    nbytes = workspace_bytes(M, K, N, max_outliers)
+    if nbytes == 0:
+        raise ValueError(f"bad shape for int8_mixed_matmul: M={M} K={K} N={N} "
+                         f"max_outliers={max_outliers}")
+    return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+
+
+def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold: float = 6.0,
+                 max_outliers: int = 256, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = the decomposed product of X [M, K] and the prepared weight."""
+    _need(X, torch.float16, "X")
+    _need(Wq, torch.int8, "Wq")
+    _need(a_w, torch.float32, "a_w")
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or a_w.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
+                         f"a_w {tuple(a_w.shape)}")
+    if workspace is None:
+        workspace = make_workspace(M, K, N, max_outliers, X.device)
+    _need(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(out, torch.float16, "out")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out")
+        if tuple(acc_out.shape) != (M, N):
+            raise ValueError("acc_out must be [M, N]")
+    _check(lib().int8_mixed_matmul(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
+                                   float(threshold), max_outliers, out.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(),
+                                   acc_out.data_ptr() if acc_out is not None else None,
+                                   _stream(X)), "int8_mixed_matmul")
+    return out
+
+
+def read_status(workspace: torch.Tensor) -> tuple[int, int]:
+    """(status of the last int8_mixed_matmul call on this workspace, its outlier count)."""
+    n = ctypes.c_int32(0)
+    rc = lib().int8mm_read_status(workspace.data_ptr(), ctypes.byref(n), _stream(workspace))
+    if rc in (1, 6):
+        raise Int8mmError(rc, "int8mm_read_status")
+    return rc, n.value
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().int8mm_timing_enable(1 if on else 0)
+
+
+def timing_read() -> tuple[float, int]:
+    """(summed main-kernel milliseconds, launches) since the last read."""
+    ms = ctypes.c_double(0.0)
+    n = _i64(0)
+    _check(lib().int8mm_timing_read(ctypes.byref(ms), ctypes.byref(n)), "int8mm_timing_read")
+    return ms.value, n.value

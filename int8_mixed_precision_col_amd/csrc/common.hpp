@@ -1,0 +1,74 @@
+// Device helpers shared by the int8mm kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+constexpr int kQMax = 127;
+constexpr float kInvQMax2 = 1.0f / 16129.0f;  // 1 / 127^2
+
+// int8 code of v under absmax constant a: round-half-to-even of 127 v / a, and 0 when
+// a == 0 ("What is 8-bit LLM quantization?", How does INT8 quantization work?: the
+// stored integer is the rounded quotient by the scale, here a / 127).
+// 127 * v is exact in fp32 for fp16 v (11-bit significand times a 7-bit integer);
+// __fdiv_rn is the IEEE correctly rounded divide and rint rounds ties to even. For
+// |v| <= a this is exactly round-half-even of the rational 127 v / a: a quotient
+// that is not a tie lies at least 2^-18 |q| away from the nearest half-integer,
+// farther than the 2^-24 |q| error of the rounded fp32 quotient.
+__device__ __forceinline__ int quant_code(float v, float a) {
+  return a == 0.0f ? 0 : static_cast<int>(__builtin_rintf(__fdiv_rn(127.0f * v, a)));
+}
+
+// Pack four codes in [-127, 127] into one little-endian dword.
+__device__ __forceinline__ unsigned pack4(int a, int b, int c, int d) {
+  return (static_cast<unsigned>(a) & 0xFFu) | ((static_cast<unsigned>(b) & 0xFFu) << 8) |
+         ((static_cast<unsigned>(c) & 0xFFu) << 16) | (static_cast<unsigned>(d) << 24);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ unsigned wave_or(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Raw buffer resource over [base, base + bytes). Loads whose offset lies outside
+// return zeros, which the kernels use for ragged tiles instead of branches.
+// bytes must be < 2^31 so that kOOB below is always out of range.
+constexpr unsigned kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ v4u buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+}
+
+}  // namespace i8mm

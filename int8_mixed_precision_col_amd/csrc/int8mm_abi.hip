@@ -1,0 +1,239 @@
+// C ABI of libint8mm.so: argument validation, workspace layout, kernel dispatch.
+// Declarations and the contract of each call are in include/int8mm.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <utility>
+#include <vector>
+
+#include "int8mm.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxK = 133144;          // 127 * 127 * K < 2^31
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxOutliers = 8192;     // LDS holds the ranked outlier list
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bad_k(int64_t K) { return K < 16 || K % 16 != 0 || K > kMaxK; }
+bool bad_n(int64_t N) { return N < 16 || N % 16 != 0 || N > kMaxMN; }
+bool bad_m(int64_t M) { return M < 1 || M > kMaxMN; }
+bool bad_outliers(int64_t mo, int64_t K) { return mo < 0 || mo > K || mo > kMaxOutliers; }
+bool bad_threshold(float t) { return isnan(t) || t < 0.0f; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Row chunks of the outlier-mask launch: enough blocks to cover the chip.
+int mask_row_chunks(int64_t M, int64_t K) {
+  const int64_t strips = (K + 63) / 64;
+  int64_t r = (1024 + strips - 1) / strips;
+  const int64_t max_r = (M + 31) / 32;
+  if (r > max_r) r = max_r;
+  if (r > 64) r = 64;
+  return r < 1 ? 1 : static_cast<int>(r);
+}
+
+struct Layout {
+  size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, wot = 0, total = 0;
+  int R = 1, o_stride = 0;
+};
+
+// Workspace: [status, count] header, then (prefill only) the row-chunk column flags,
+// a_x, Xq, Xo and WoT, each 256-byte aligned.
+Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+  Layout L;
+  size_t off = 256;
+  if (i8mm::decode_supported(M, K)) {
+    L.total = off;
+    return L;
+  }
+  const size_t W = (K + 31) / 32;
+  L.R = mask_row_chunks(M, K);
+  L.o_stride = static_cast<int>((max_outliers + 15) & ~int64_t(15));
+  L.partial = off; off += round256(size_t(L.R) * W * 4);
+  L.a_x = off;     off += round256(size_t(M) * 4);
+  L.xq = off;      off += round256(size_t(M) * K);
+  L.xo = off;      off += round256(size_t(M) * L.o_stride * 2);
+  L.wot = off;     off += round256(size_t(N) * L.o_stride * 2);
+  L.total = off;
+  return L;
+}
+
+// Optional event timing of the main kernel.
+bool g_timing = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+size_t g_events_used = 0;
+
+int timing_begin(hipStream_t s) {
+  if (!g_timing) return INT8MM_OK;
+  if (g_events_used == g_events.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return INT8MM_E_HIP;
+    if (hipEventCreate(&b) != hipSuccess) return INT8MM_E_HIP;
+    g_events.emplace_back(a, b);
+  }
+  return hipEventRecord(g_events[g_events_used].first, s) == hipSuccess ? INT8MM_OK : INT8MM_E_HIP;
+}
+
+int timing_end(hipStream_t s) {
+  if (!g_timing) return INT8MM_OK;
+  if (hipEventRecord(g_events[g_events_used].second, s) != hipSuccess) return INT8MM_E_HIP;
+  ++g_events_used;
+  return INT8MM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int int8_prepare_weight(const void* W, int64_t K, int64_t N, int w_layout, int8_t* Wq,
+                        float* w_absmax, hipStream_t stream) {
+  if (!W || !Wq || !w_absmax) return INT8MM_E_NULL;
+  if (bad_k(K) || bad_n(N) || (w_layout != 0 && w_layout != 1)) return INT8MM_E_SHAPE;
+  if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_absmax)) return INT8MM_E_ALIGN;
+  return hip_status(i8mm::launch_prepare_weight(static_cast<const _Float16*>(W), int(K), int(N),
+                                                w_layout, Wq, w_absmax, stream));
+}
+
+int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t* Xq,
+                    float* x_absmax, uint32_t* outlier_mask, int32_t* outlier_idx,
+                    int32_t* n_outliers, int64_t max_outliers, hipStream_t stream) {
+  if (!X || !Xq || !x_absmax || !outlier_mask || !n_outliers) return INT8MM_E_NULL;
+  if (max_outliers > 0 && !outlier_idx) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
+  if (!aligned16(X) || !aligned16(Xq) || !aligned16(x_absmax) || !aligned16(outlier_mask) ||
+      !aligned16(n_outliers) || (outlier_idx && !aligned16(outlier_idx)))
+    return INT8MM_E_ALIGN;
+  const _Float16* x = static_cast<const _Float16*>(X);
+  hipError_t e = i8mm::launch_outlier_mask(x, int(M), int(K), threshold, 1, outlier_mask, stream);
+  if (e != hipSuccess) return INT8MM_E_HIP;
+  i8mm::QuantRowsArgs q{};
+  q.X = x; q.M = int(M); q.K = int(K);
+  q.partial = outlier_mask; q.R = 1;
+  q.Xq = Xq; q.a_x = x_absmax;
+  q.idx_out = max_outliers > 0 ? outlier_idx : nullptr;
+  q.count_out = n_outliers; q.status_out = nullptr;
+  q.max_outliers = int(max_outliers);
+  return hip_status(i8mm::launch_quant_rows(q, stream));
+}
+
+size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+  if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return 0;
+  return layout(M, K, N, max_outliers).total;
+}
+
+int int8_mixed_matmul_is_decode(int64_t M, int64_t K) {
+  return i8mm::decode_supported(M, K) ? 1 : 0;
+}
+
+int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                      const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
+                      void* Y, void* workspace, size_t workspace_bytes, int32_t* acc_i32,
+                      hipStream_t stream) {
+  if (!X || !Wq || !w_absmax || !Y || !workspace) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
+      !aligned16(workspace) || (acc_i32 && !aligned16(acc_i32)))
+    return INT8MM_E_ALIGN;
+  const Layout L = layout(M, K, N, max_outliers);
+  if (workspace_bytes < L.total) return INT8MM_E_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+  const _Float16* x = static_cast<const _Float16*>(X);
+  _Float16* y = static_cast<_Float16*>(Y);
+  int rc;
+
+  if (i8mm::decode_supported(M, K)) {
+    i8mm::DecodeArgs d{};
+    d.X = x; d.M = int(M); d.K = int(K); d.t = threshold;
+    d.Wq = Wq; d.a_w = w_absmax; d.N = int(N);
+    d.max_outliers = int(max_outliers);
+    d.Y = y; d.acc_out = acc_i32; d.status = status;
+    if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
+    if (i8mm::launch_decode(d, stream) != hipSuccess) return INT8MM_E_HIP;
+    return timing_end(stream);
+  }
+
+  uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
+  float* a_x = reinterpret_cast<float*>(ws + L.a_x);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+  _Float16* xo = reinterpret_cast<_Float16*>(ws + L.xo);
+  _Float16* wot = reinterpret_cast<_Float16*>(ws + L.wot);
+
+  if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
+    return INT8MM_E_HIP;
+  i8mm::QuantRowsArgs q{};
+  q.X = x; q.M = int(M); q.K = int(K);
+  q.partial = partial; q.R = L.R;
+  q.Xq = xq; q.a_x = a_x;
+  q.idx_out = nullptr; q.count_out = status + 1; q.status_out = status;
+  q.max_outliers = int(max_outliers);
+  q.Xo = xo; q.o_stride = L.o_stride;
+  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
+  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
+
+  i8mm::GemmArgs g{};
+  g.Wq = Wq; g.Xq = xq; g.M = int(M); g.N = int(N); g.K = int(K);
+  g.a_x = a_x; g.a_w = w_absmax;
+  g.Xo = xo; g.WoT = wot; g.o_stride = L.o_stride;
+  g.count = status + 1; g.max_outliers = int(max_outliers);
+  g.Y = y; g.acc_out = acc_i32;
+  if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
+  if (i8mm::launch_gemm(g, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream);
+}
+
+int int8mm_read_status(const void* workspace, int32_t* n_outliers, hipStream_t stream) {
+  if (!workspace) return INT8MM_E_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return INT8MM_E_HIP;
+  int32_t h[2] = {0, 0};
+  if (hipMemcpy(h, workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return INT8MM_E_HIP;
+  if (n_outliers) *n_outliers = h[1];
+  return h[0];
+}
+
+const char* int8mm_strerror(int code) {
+  switch (code) {
+    case INT8MM_OK: return "ok";
+    case INT8MM_E_NULL: return "a required pointer is NULL";
+    case INT8MM_E_SHAPE: return "bad shape: need M >= 1, K and N multiples of 16 (>= 16), "
+                                "K <= 133144, M and N <= 2^24, 0 <= max_outliers <= min(K, 8192), "
+                                "layout 0 or 1";
+    case INT8MM_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case INT8MM_E_THRESHOLD: return "threshold is NaN or negative";
+    case INT8MM_E_WORKSPACE: return "workspace smaller than int8_mixed_matmul_workspace_bytes()";
+    case INT8MM_E_HIP: return "HIP runtime error or failed kernel launch";
+    case INT8MM_E_TOO_MANY_OUTLIERS: return "more outlier columns than max_outliers (Y is NaN)";
+    default: return "unknown int8mm status code";
+  }
+}
+
+int int8mm_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return INT8MM_OK;
+}
+
+int int8mm_timing_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return INT8MM_E_NULL;
+  double sum = 0.0;
+  for (size_t i = 0; i < g_events_used; ++i) {
+    if (hipEventSynchronize(g_events[i].second) != hipSuccess) return INT8MM_E_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_events[i].first, g_events[i].second) != hipSuccess)
+      return INT8MM_E_HIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int64_t>(g_events_used);
+  g_events_used = 0;
+  return INT8MM_OK;
+}
+
+}  // extern "C"

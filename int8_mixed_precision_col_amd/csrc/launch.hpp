@@ -1,0 +1,69 @@
+// Host-side launchers of the int8mm kernels (internal to libint8mm.so).
+// Each returns hipSuccess or the launch error; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+// Weight conversion: W fp16 [K, N] (layout 0) or [N, K] (layout 1) -> Wq [N, K], a_w [N].
+hipError_t launch_prepare_weight(const _Float16* W, int K, int N, int layout, int8_t* Wq,
+                                 float* a_w, hipStream_t s);
+
+// Column outlier flags: partial[rc * W + w] for row chunk rc < R, word w < W = ceil(K/32).
+hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
+                               uint32_t* partial, hipStream_t s);
+
+struct QuantRowsArgs {
+  const _Float16* X;
+  int M, K;
+  const uint32_t* partial;  // [R][W] column flags from launch_outlier_mask
+  int R;
+  int8_t* Xq;
+  float* a_x;
+  int32_t* idx_out;     // [max_outliers], nullable when max_outliers == 0
+  int32_t* count_out;   // [1]
+  int32_t* status_out;  // [1], nullable
+  int max_outliers;
+  _Float16* Xo;         // nullable: [M][o_stride] fp16 outlier activations
+  int o_stride;         // multiple of 16, >= max_outliers
+  const int8_t* Wq;     // for the WoT gather (nullable = no gather)
+  const float* a_w;
+  int N;
+  _Float16* WoT;        // [N][o_stride] fp16 dequantized outlier weight rows
+};
+hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
+
+struct GemmArgs {
+  const int8_t* Wq;   // [N][K]
+  const int8_t* Xq;   // [M][K]
+  int M, N, K;
+  const float* a_x;
+  const float* a_w;
+  const _Float16* Xo;   // [M][o_stride]
+  const _Float16* WoT;  // [N][o_stride]
+  int o_stride;
+  const int32_t* count;
+  int max_outliers;
+  _Float16* Y;          // [M][N]
+  int32_t* acc_out;     // nullable [M][N]
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const _Float16* X;  // [M][K]
+  int M, K;
+  float t;
+  const int8_t* Wq;   // [N][K]
+  const float* a_w;
+  int N;
+  int max_outliers;
+  _Float16* Y;
+  int32_t* acc_out;   // nullable
+  int32_t* status;    // [0] = status, [1] = outlier count
+};
+bool decode_supported(int64_t M, int64_t K);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace i8mm

@@ -1,0 +1,230 @@
+// Outlier detection and vector-wise row quantization of the activations.
+//
+// "8-bit Matrix Multiplication for Large Language Models", Summary & Methodology
+// Analysis, and "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale",
+// Abstract: the emergent outlier feature dimensions (columns of X) are isolated and
+// multiplied in 16 bit; everything else is quantized with one normalization constant
+// per inner product. "Compress your LLMs", Vector-wise quantization: one constant per
+// row of the input matrix. A column j is an outlier when some row has |X[i,j]| >= t;
+// the row constant is the absmax over the remaining columns.
+//
+// Two launches, because every row needs the complete column mask before it can pick
+// its constant:
+//   k_outlier_mask  column strips x row chunks -> per-chunk column flag words (no
+//                   atomics and no pre-zeroed memory: every word is written).
+//   k_quant_rows    ORs the chunk flags, ranks the outlier columns with a block scan,
+//                   then one wave per row: absmax over kept columns, quantize, store
+//                   Xq; gathers the fp16 outlier activations Xo. Extra blocks gather
+//                   the dequantized int8 weight rows of the outlier columns, WoT.
+// Both are HBM-bound streaming kernels (X read, Xq written).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8mm {
+
+// Block (strip, chunk): 64 columns x rows [chunk*rpc, +rpc). 8 threads x 16 B per row.
+__global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict__ X, int M, int K,
+                                                      float t, int rpc,
+                                                      uint32_t* __restrict__ partial, int W) {
+  const int tid = threadIdx.x;
+  const int cg = tid & 7;
+  const int col0 = blockIdx.x * 64 + cg * 8;
+  const int r_begin = blockIdx.y * rpc;
+  const int r_end = min(M, r_begin + rpc);
+  unsigned flags = 0;
+  if (col0 < K) {
+#pragma unroll 8
+    for (int r = r_begin + (tid >> 3); r < r_end; r += 32) {
+      v8h v = *reinterpret_cast<const v8h*>(X + static_cast<size_t>(r) * K + col0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        flags |= static_cast<unsigned>(fabsf(static_cast<float>(v[e])) >= t) << e;
+    }
+  }
+  flags |= __shfl_xor(flags, 8, 64);
+  flags |= __shfl_xor(flags, 16, 64);
+  flags |= __shfl_xor(flags, 32, 64);
+  __shared__ unsigned s[4][8];
+  if ((tid & 63) < 8) s[tid >> 6][cg] = flags;
+  __syncthreads();
+  if (tid < 2) {
+    unsigned word = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = tid * 4 + g;
+      word |= (s[0][c] | s[1][c] | s[2][c] | s[3][c]) << (8 * g);
+    }
+    const int w = blockIdx.x * 2 + tid;
+    if (w < W) partial[static_cast<size_t>(blockIdx.y) * W + w] = word;
+  }
+}
+
+// One wave quantizes one row. CH > 0: the row is held in registers (CH chunks of 8
+// halves per lane, K <= 512 * CH) and read once; CH == 0: streamed twice.
+template <int CH>
+__device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, int K,
+                                              const uint32_t* words, int8_t* __restrict__ xq,
+                                              float* a_x_row, int lane) {
+  const int nchunk = K >> 3;
+  auto chunk_mask = [&](int c) -> unsigned { return (words[c >> 2] >> ((c & 3) << 3)) & 0xFFu; };
+  auto store_codes = [&](int c, const v8h& v, unsigned mb, float m) {
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = ((mb >> e) & 1u) ? 0 : quant_code(v[e], m);
+    v2u o;
+    o[0] = pack4(q[0], q[1], q[2], q[3]);
+    o[1] = pack4(q[4], q[5], q[6], q[7]);
+    *reinterpret_cast<v2u*>(xq + c * 8) = o;
+  };
+  float m = 0.0f;
+  if constexpr (CH > 0) {
+    v8h v[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) v[i] = *reinterpret_cast<const v8h*>(xr + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) {
+        const unsigned mb = chunk_mask(c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((mb >> e) & 1u)) m = fmaxf(m, fabsf(static_cast<float>(v[i][e])));
+      }
+    }
+    m = wave_max(m);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) store_codes(c, v[i], chunk_mask(c), m);
+    }
+  } else {
+    for (int c = lane; c < nchunk; c += 64) {
+      const v8h v = *reinterpret_cast<const v8h*>(xr + c * 8);
+      const unsigned mb = chunk_mask(c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((mb >> e) & 1u)) m = fmaxf(m, fabsf(static_cast<float>(v[e])));
+    }
+    m = wave_max(m);
+    for (int c = lane; c < nchunk; c += 64)
+      store_codes(c, *reinterpret_cast<const v8h*>(xr + c * 8), chunk_mask(c), m);
+  }
+  if (lane == 0) *a_x_row = m;
+}
+
+// Blocks [0, nrow): rows 4b..4b+3 (one wave each). Blocks [nrow, nrow + ngather): WoT
+// rows n = 256 (b - nrow) + tid. Dynamic LDS: W mask words, then o_lds ranked columns.
+template <int CH>
+__global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int o_lds, int nrow) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* words = lds;
+  int* idx_s = reinterpret_cast<int*>(lds + W);
+  __shared__ int wave_tot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // 1. column mask = OR of the row-chunk flags
+  for (int w = tid; w < W; w += 256) {
+    uint32_t v = 0;
+    for (int rc = 0; rc < a.R; ++rc) v |= a.partial[static_cast<size_t>(rc) * W + w];
+    words[w] = v;
+  }
+  __syncthreads();
+  // 2. rank the outlier columns: thread t owns words [t*per, (t+1)*per)
+  const int per = (W + 255) / 256;
+  const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(words[w]);
+  const int incl = wave_inclusive_sum(mine);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = incl - mine;
+  for (int i = 0; i < wave; ++i) before += wave_tot[i];
+  const int count = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  for (int w = w0, r = before; w < w1; ++w) {
+    uint32_t bits = words[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (r < o_lds) idx_s[r] = w * 32 + b;
+      ++r;
+    }
+  }
+  __syncthreads();
+
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      a.count_out[0] = count;
+      if (a.status_out) a.status_out[0] = count > a.max_outliers ? 7 : 0;
+    }
+    if (a.idx_out)
+      for (int r = tid; r < min(count, a.max_outliers); r += 256) a.idx_out[r] = idx_s[r];
+  }
+  // outlier columns actually carried (padded to the 16-wide fp16 MFMA step)
+  const int o_pad = min((count + 15) & ~15, a.o_stride);
+
+  if (static_cast<int>(blockIdx.x) < nrow) {
+    const int row = blockIdx.x * 4 + wave;
+    if (row >= a.M) return;
+    const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
+    quant_one_row<CH>(xr, a.K, words, a.Xq + static_cast<size_t>(row) * a.K, a.a_x + row, lane);
+    if (a.Xo) {
+      _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
+      for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
+    }
+  } else {
+    // WoT[n, r] = fp16(Wq[n, O_r] * a_w[n] / 127): the outlier columns' weights,
+    // dequantized from the int8 copy that is the only weight kept in memory.
+    const int n = (blockIdx.x - nrow) * 256 + tid;
+    if (n >= a.N) return;
+    const float aw = a.a_w[n];
+    const int8_t* wr = a.Wq + static_cast<size_t>(n) * a.K;
+    _Float16* dst = a.WoT + static_cast<size_t>(n) * a.o_stride;
+    for (int r0 = 0; r0 < o_pad; r0 += 8) {
+      v8h o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        o[e] = r < count ? static_cast<_Float16>(
+                               __fdiv_rn(static_cast<float>(wr[idx_s[r]]) * aw, 127.0f))
+                         : _Float16(0);
+      }
+      *reinterpret_cast<v8h*>(dst + r0) = o;
+    }
+  }
+}
+
+hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
+                               uint32_t* partial, hipStream_t s) {
+  const int W = (K + 31) / 32;
+  const int rpc = (M + R - 1) / R;
+  hipLaunchKernelGGL(k_outlier_mask, dim3((K + 63) / 64, R), dim3(256), 0, s, X, M, K, t, rpc,
+                     partial, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s) {
+  const int W = (a.K + 31) / 32;
+  const int o_lds = a.o_stride > a.max_outliers ? a.o_stride : a.max_outliers;
+  const size_t lds = static_cast<size_t>(W + o_lds) * 4;
+  const int nrow = (a.M + 3) / 4;
+  const int ngather = a.WoT ? (a.N + 255) / 256 : 0;
+  const dim3 grid(nrow + ngather), block(256);
+  const int per_lane = (a.K / 8 + 63) / 64;
+#define I8MM_QR(CHV) hipLaunchKernelGGL(k_quant_rows<CHV>, grid, block, lds, s, a, W, o_lds, nrow)
+  if (per_lane <= 1) I8MM_QR(1);
+  else if (per_lane <= 2) I8MM_QR(2);
+  else if (per_lane <= 4) I8MM_QR(4);
+  else if (per_lane <= 8) I8MM_QR(8);
+  else if (per_lane <= 16) I8MM_QR(16);
+  else if (per_lane <= 24) I8MM_QR(24);
+  else if (per_lane <= 32) I8MM_QR(32);
+  else if (per_lane <= 40) I8MM_QR(40);
+  else I8MM_QR(0);
+#undef I8MM_QR
+  return hipGetLastError();
+}
+
+}  // namespace i8mm

@@ -1,0 +1,112 @@
+"""Host-side checks of libint8mm.so: it loads, exports every declared symbol, and
+rejects bad arguments synchronously before any HIP call (no GPU needed).
+
+The pointers below are fake, 16-byte-aligned addresses: every call here fails
+validation, which the library does before it touches a pointer or the runtime.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from int8_mixed_precision_col_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8mm.h")
+
+P = 0x10000          # aligned fake device address
+UNALIGNED = 0x10008
+OK, E_NULL, E_SHAPE, E_ALIGN, E_THR, E_WS = 0, 1, 2, 3, 4, 5
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libint8mm.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:int8_|int8mm_)\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_covers_codes(L):
+    texts = {c: binding.strerror(c) for c in range(0, 8)}
+    assert texts[0] == "ok"
+    assert len(set(texts.values())) == 8
+    assert "unknown" in binding.strerror(99)
+
+
+def mm(L, X=P, M=64, K=256, Wq=P, aw=P, N=256, t=6.0, mo=16, Y=P, ws=P, wsb=1 << 30, acc=None):
+    return L.int8_mixed_matmul(X, M, K, Wq, aw, N, t, mo, Y, ws, wsb, acc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), E_NULL), (dict(Wq=None), E_NULL), (dict(aw=None), E_NULL),
+    (dict(Y=None), E_NULL), (dict(ws=None), E_NULL),
+    (dict(M=0), E_SHAPE), (dict(K=0), E_SHAPE), (dict(K=24), E_SHAPE), (dict(N=8), E_SHAPE),
+    (dict(N=40), E_SHAPE), (dict(K=133152), E_SHAPE), (dict(M=1 << 25), E_SHAPE),
+    (dict(mo=-1), E_SHAPE), (dict(mo=257), E_SHAPE), (dict(K=16384, mo=8193), E_SHAPE),
+    (dict(t=-1.0), E_THR), (dict(t=math.nan), E_THR),
+    (dict(X=UNALIGNED), E_ALIGN), (dict(Y=UNALIGNED), E_ALIGN), (dict(ws=UNALIGNED), E_ALIGN),
+    (dict(acc=UNALIGNED), E_ALIGN),
+    (dict(wsb=0), E_WS), (dict(M=4096, K=4096, N=4096, wsb=1 << 20), E_WS),
+])
+def test_mixed_matmul_rejects(L, kw, code):
+    assert mm(L, **kw) == code
+
+
+def test_quant_rows_rejects(L):
+    q = L.int8_quant_rows
+    assert q(None, 4, 32, 6.0, P, P, P, P, P, 4, None) == E_NULL
+    assert q(P, 4, 32, 6.0, P, P, P, None, P, 4, None) == E_NULL   # idx needed when mo > 0
+    assert q(P, 4, 30, 6.0, P, P, P, P, P, 4, None) == E_SHAPE
+    assert q(P, 4, 32, 6.0, P, P, P, P, P, 33, None) == E_SHAPE
+    assert q(P, 4, 32, -0.5, P, P, P, P, P, 4, None) == E_THR
+    assert q(P, 4, 32, 6.0, UNALIGNED, P, P, P, P, 4, None) == E_ALIGN
+
+
+def test_prepare_weight_rejects(L):
+    pw = L.int8_prepare_weight
+    assert pw(None, 32, 32, 0, P, P, None) == E_NULL
+    assert pw(P, 32, 33, 0, P, P, None) == E_SHAPE
+    assert pw(P, 32, 32, 2, P, P, None) == E_SHAPE
+    assert pw(P, 32, 32, 1, UNALIGNED, P, None) == E_ALIGN
+
+
+def test_workspace_sizes(L):
+    ws = L.int8_mixed_matmul_workspace_bytes
+    assert ws(0, 64, 64, 16) == 0 and ws(64, 64, 64, 65) == 0
+    # decode path: header only
+    assert L.int8_mixed_matmul_is_decode(8, 4096) == 1 and ws(8, 4096, 4096, 256) == 256
+    assert L.int8_mixed_matmul_is_decode(16, 1024) == 1
+    assert L.int8_mixed_matmul_is_decode(17, 1024) == 0
+    assert L.int8_mixed_matmul_is_decode(8, 8192) == 0          # M*K above the LDS budget
+    # prefill: at least Xq + a_x + Xo + WoT
+    M, K, N, mo = 2048, 4096, 16384, 256
+    b = ws(M, K, N, mo)
+    assert b >= M * K + 4 * M + 2 * M * mo + 2 * N * mo
+    assert b < M * K + 4 * M + 2 * M * mo + 2 * N * mo + (1 << 20)
+    assert ws(M, K, N, 0) < b and ws(M + 1, K, N, mo) > b
+    assert b % 256 == 0
+
+
+def test_timing_read_without_launches(L):
+    ms, n = binding.timing_read()
+    assert (ms, n) == (0.0, 0)
+    assert L.int8mm_timing_read(None, None) == E_NULL

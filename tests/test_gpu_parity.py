@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: Wq, a_w, outlier mask / index list / count, a_x, Xq and the int32
+accumulators. Within TOL of max|Y_oracle|: the fp16 output. Shapes span several
+tiles with ragged tails on both dispatch paths (decode kernel for M <= 16, and
+mask -> quant -> MFMA GEMM otherwise, in its small- and large-tile configurations).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_mixed_precision_col_amd import binding, inputs
+from tests.gpu_util import TOL, announce, check_y, dev, grid_weight, host
+
+pytestmark = pytest.mark.gpu
+INF = float("inf")
+
+
+def planted(seed, M, K, n_dims=4, lo=15.0, hi=60.0, frac=0.75):
+    wl = inputs.Workload(f"p{seed}", M, K, 16, n_dims, lo, hi, frac, 0.02, seed=seed)
+    X, _ = inputs.make_x(wl)
+    return X
+
+
+def weight(seed, K, N, std=0.02):
+    rng = np.random.default_rng([seed, 7])
+    return (rng.standard_normal((K, N), dtype=np.float32) * np.float32(std)).astype(np.float16)
+
+
+# ------------------------------------------------------------------ prepare
+
+@pytest.mark.parametrize("K,N,layout", [(1024, 1024, 0), (1040, 528, 0), (1040, 528, 1),
+                                        (16, 16, 0), (4112, 80, 1)])
+def test_prepare_weight_bit_exact(K, N, layout):
+    announce(f"prepare_weight K={K} N={N} layout={layout}")
+    W = weight(K + N, K, N)
+    W[:, 3] = 0                         # all-zero column: constant 0, codes 0
+    Wq_ref, aw_ref = oracle.prepare_weight(W)
+    src = W if layout == 0 else np.ascontiguousarray(W.T)
+    Wq, aw = binding.prepare_weight(dev(src), layout)
+    assert np.array_equal(host(aw), aw_ref)
+    assert np.array_equal(host(Wq), Wq_ref)
+
+
+# ------------------------------------------------------------------ quant rows
+
+def _quant_case(X, t, mo):
+    ref = oracle.quant_rows(X, t)
+    got = binding.quant_rows(dev(X), t, mo)
+    count = int(host(got["count"])[0])
+    assert count == ref["count"]
+    assert np.array_equal(host(got["mask"]).view(np.uint32), oracle.mask_words(ref["mask"]))
+    n = min(count, mo)
+    assert np.array_equal(host(got["idx"])[:n], ref["idx"][:n])
+    assert np.array_equal(host(got["a_x"]), ref["a_x"])
+    assert np.array_equal(host(got["Xq"]), ref["Xq"])
+    return ref
+
+
+@pytest.mark.parametrize("M,K,t,mo", [
+    (16, 1024, 6.0, 256), (300, 1040, 6.0, 256), (7, 20480, 6.0, 256),
+    (3, 33024, 6.0, 64), (129, 4096, INF, 16), (33, 528, 0.0, 528), (65, 1024, 6.0, 2),
+])
+def test_quant_rows_bit_exact(M, K, t, mo):
+    announce(f"quant_rows M={M} K={K} t={t} max_outliers={mo}")
+    X = planted(M * 31 + K, M, K, n_dims=5)
+    _quant_case(X, t, mo)
+
+
+def test_quant_rows_adversarial():
+    announce("quant_rows adversarial ties / zero rows / all-outlier rows")
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((37, 96)).astype(np.float32)
+    X[:, 10] = 6.0                       # exactly the threshold: outlier
+    X[:, 11] = np.float16(5.99609375)    # largest fp16 below 6: not an outlier
+    X[2, :] = 0.0                        # zero row
+    X[3, :] = 0.0
+    X[3, 40] = 9.0                       # row whose only nonzero is in an outlier column
+    X[4, :] = 2.5                        # constant row: every code 127
+    X[5, 50] = -6.0
+    ref = _quant_case(X.astype(np.float16), 6.0, 16)
+    assert 10 in ref["idx"] and 11 not in ref["idx"] and ref["a_x"][3] == 0
+
+
+# ------------------------------------------------------------------ mixed matmul
+
+def _mixed(X, W, t, mo=256, workspace=None):
+    Wq_ref, aw_ref = oracle.prepare_weight(W)
+    ref = oracle.mixed_matmul(X, Wq_ref, aw_ref, t)
+    Wq, aw = binding.prepare_weight(dev(W))
+    M, N = X.shape[0], W.shape[1]
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = binding.mixed_matmul(dev(X), Wq, aw, t, mo, workspace=workspace, acc_out=acc)
+    return ref, host(Y), host(acc)
+
+
+CASES = [
+    # (M, K, N): decode kernel
+    (16, 1024, 1024), (5, 1040, 528), (8, 4096, 4096), (1, 32, 16), (16, 2048, 80),
+    # prefill, small tiles
+    (300, 1040, 528), (17, 256, 4112), (64, 8192, 256), (1, 12288, 64),
+    # prefill, large tiles
+    (1040, 1040, 16400),
+]
+
+
+@pytest.mark.parametrize("M,K,N", CASES)
+def test_mixed_matmul_parity(M, K, N):
+    path = "decode" if binding.is_decode(M, K) else "prefill"
+    announce(f"mixed_matmul {path} M={M} K={K} N={N}")
+    X = planted(M + 3 * K + N, M, K, n_dims=3)
+    W = weight(M + K, K, N)
+    ref, Y, acc = _mixed(X, W, 6.0)
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 1024, 256), (200, 1040, 528)])
+def test_zero_outlier_invariant(M, K, N):
+    """t = +inf: no outlier columns; Y is the dequantized int8 product."""
+    announce(f"zero-outlier invariant M={M} K={K} N={N}")
+    X = planted(11 + M, M, K, n_dims=2)
+    W = weight(12 + M, K, N)
+    ref, Y, acc = _mixed(X, W, INF)
+    assert ref["count"] == 0
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["y_int8"].astype(np.float16))
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 512, 128), (96, 528, 272)])
+def test_all_outlier_invariant(M, K, N):
+    """t = 0: every column is an outlier; with a lossless int8 weight, Y = fp16(X @ W)."""
+    announce(f"all-outlier invariant M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K)
+    X = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    W = grid_weight(rng, K, N)
+    ref, Y, acc = _mixed(X, W, 0.0, mo=K)
+    assert ref["count"] == K and np.all(acc == 0)
+    textbook = (X.astype(np.float64) @ W.astype(np.float64)).astype(np.float16)
+    check_y(Y, textbook)
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 1024, 256), (100, 1024, 256)])
+def test_outlier_overflow_sets_status_and_nan(M, K, N):
+    announce(f"outlier overflow M={M} K={K} N={N}")
+    X = planted(21 + M, M, K, n_dims=5)
+    W = weight(22, K, N)
+    Wq, aw = binding.prepare_weight(dev(W))
+    ws = binding.make_workspace(M, K, N, 2)
+    Y = binding.mixed_matmul(dev(X), Wq, aw, 6.0, 2, workspace=ws)
+    status, count = binding.read_status(ws)
+    assert status == 7 and count >= 5
+    assert torch.isnan(Y).all().item()
+    # the same workspace, enough capacity: status clears
+    ws2 = binding.make_workspace(M, K, N, 16)
+    binding.mixed_matmul(dev(X), Wq, aw, 6.0, 16, workspace=ws2)
+    assert binding.read_status(ws2) == (0, count)
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 4096, 4096), (700, 2064, 1040)])
+def test_deterministic(M, K, N):
+    announce(f"determinism M={M} K={K} N={N}")
+    X = dev(planted(31, M, K))
+    Wq, aw = binding.prepare_weight(dev(weight(32, K, N)))
+    a = binding.mixed_matmul(X, Wq, aw, 6.0)
+    b = binding.mixed_matmul(X, Wq, aw, 6.0)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace sized for the larger call serves a smaller one afterwards."""
+    announce("workspace reuse")
+    big = binding.make_workspace(512, 2048, 1024, 256)
+    for (M, K, N) in [(512, 2048, 1024), (40, 1040, 528)]:
+        X = planted(M, M, K)
+        W = weight(M, K, N)
+        ref, Y, acc = _mixed(X, W, 6.0, workspace=big)
+        assert np.array_equal(acc, ref["acc"])
+        check_y(Y, ref["Y"])
+
+
+def test_timing_hook_counts_main_kernel():
+    announce("timing hook")
+    X = dev(planted(41, 64, 1024))
+    Wq, aw = binding.prepare_weight(dev(weight(42, 1024, 512)))
+    binding.timing_read()
+    binding.timing_enable(True)
+    try:
+        for _ in range(3):
+            binding.mixed_matmul(X, Wq, aw, 6.0)
+        ms, n = binding.timing_read()
+    finally:
+        binding.timing_enable(False)
+    assert n == 3 and ms > 0
