@@ -30,6 +30,22 @@ __device__ __forceinline__ int quant_code(float v, float a) {
   return a == 0.0f ? 0 : static_cast<int>(__builtin_rintf(__fdiv_rn(127.0f * v, a)));
 }
 
+// Per-row reciprocal for quant_code_fast: 127 / a correctly rounded, 0 for a == 0.
+__device__ __forceinline__ float quant_scale(float a) {
+  return a == 0.0f ? 0.0f : __fdiv_rn(127.0f, a);
+}
+
+// quant_code without a divide per element. With r = quant_scale(a), t = v * r is
+// within 127 * 2^-23 < 2^-16 of the exact quotient 127 v / a, so whenever t lies
+// farther than 2^-15 from a half-integer, rint(t) is already the exact
+// round-half-even; only such near-ties fall back to the correctly rounded divide.
+__device__ __forceinline__ int quant_code_fast(float v, float a, float r) {
+  const float t = v * r;
+  const float q0 = __builtin_rintf(t);
+  if (__builtin_expect(fabsf(t - q0) <= 0.5f - 0x1p-15f, 1)) return static_cast<int>(q0);
+  return quant_code(v, a);
+}
+
 // Pack four codes in [-127, 127] into one little-endian dword.
 __device__ __forceinline__ unsigned pack4(int a, int b, int c, int d) {
   return (static_cast<unsigned>(a) & 0xFFu) | ((static_cast<unsigned>(b) & 0xFFu) << 8) |

@@ -1,0 +1,294 @@
+// The int8 GEMM with the outlier fp16 product and the dequantizing epilogue.
+//
+// acc[m, n] = sum_k Xq[m, k] Wq[n, k]  (exact int32; "Compress your LLMs",
+//   Mixed-precision decomposition: 8-bit matrix multiplication for the non-outlier
+//   dimensions),
+// Y[m, n]   = fp16( acc * a_x[m] * a_w[n] / 127^2              (outer-product dequant,
+//                   "8-bit Matrix Multiplication for Large Language Models", Summary &
+//                   Methodology Analysis)
+//                 + sum_r Xo[m, r] WoT[n, r] )                  (16-bit product over the
+//                   outlier columns, summed into the same fp16 output)
+//
+// gfx950 design. Both operands are K-contiguous, so a block computes D = Wq_tile *
+// Xq_tile^T with v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with 16 consecutive K
+// bytes of each operand, and the A/B roles are chosen so that every lane ends up
+// holding 4 consecutive output columns n of one row m (8-byte fp16 stores).
+// A block of WGN x WGM waves owns a TN x TM tile; each wave a (TN/WGN) x (TM/WGM)
+// sub-tile of 32x32 blocks whose int32 accumulators live in registers.
+// K is walked in BK-byte slabs through a ring of STAGES LDS buffers filled by
+// global_load_lds_dwordx4 (global memory straight into LDS, no VGPR staging): rows
+// past the tile edge are clamped to the last row (their outputs are discarded),
+// chunks past the end of K read a 16-byte zero constant, and each lane fetches the
+// global 16-byte chunk that belongs at its LDS slot under an XOR swizzle, so that the
+// ds_read_b128 fragment reads are free of bank conflicts. Slab kt + STAGES - 1 is in
+// flight while slab kt is multiplied; one barrier per slab.
+// The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, reading the
+// small Xo / WoT fragments straight from global memory (L2-resident), accumulating
+// on top of the already dequantized fp32 values before the single rounding to fp16.
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8mm {
+
+template <int TN_, int TM_, int BK_, int WGN_, int WGM_, int STAGES_>
+struct GemmCfg {
+  static constexpr int TN = TN_, TM = TM_, BK = BK_, WGN = WGN_, WGM = WGM_, STAGES = STAGES_;
+  static constexpr int NW = WGN * WGM, NT = NW * 64;
+  static constexpr int WTN = TN / WGN, WTM = TM / WGM;
+  static constexpr int BN = WTN / 32, BM = WTM / 32;
+  static constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
+  static constexpr int A_BYTES = TN * BK, B_BYTES = TM * BK;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int AI = A_BYTES / (1024 * NW);    // 1 KB DMA instructions per wave, A
+  static constexpr int BI = B_BYTES / (1024 * NW);    // ... and B
+  static_assert(AI * 1024 * NW == A_BYTES && BI * 1024 * NW == B_BYTES, "tile / wave mismatch");
+  static_assert(BK % 32 == 0 && WTN % 32 == 0 && WTM % 32 == 0, "shape");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+};
+
+// XOR swizzle of the 16-byte chunk index within an LDS row. For the fragment reads
+// (lanes 0..31 read rows r0..r0+31 at one chunk, lanes 32..63 the next chunk) every
+// group of 8 lanes hits 8 distinct 16-byte slots of a 128-byte window and every group
+// of 16 lanes 16 distinct slots of a 256-byte window.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+  else return (r ^ (r >> 1)) & 7;
+}
+template <int BK>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * BK + 16 * (c ^ swz<BK / 16>(r));
+}
+
+// Block -> output tile. The hardware hands workgroup b to XCD b % 8; renumber so that
+// each XCD owns a contiguous run of tiles, then walk the run in groups of group_m
+// m-tiles per n-tile so that concurrently running tiles on one XCD share operand
+// slabs in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int group_m, int& tn,
+                                        int& tm) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nblocks >> 3, extra = nblocks & 7;
+  const int pid =
+      xcd < extra ? xcd * (per + 1) + local : extra * (per + 1) + (xcd - extra) * per + local;
+  const int tiles_n = nblocks / tiles_m;
+  const int per_group = group_m * tiles_n;
+  const int grp = pid / per_group;
+  const int first_m = grp * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int in = pid - grp * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+#define I8MM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Source of the K-tail chunks: multiplying by zeros adds nothing to the int32 sums.
+__device__ __attribute__((aligned(16))) const int kZero16[4] = {0, 0, 0, 0};
+
+// Waits until at most `pending` of this thread's buffer loads are outstanding and all
+// its LDS reads are done, then joins the block barrier. The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+template <int PENDING>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(PENDING >= 0 && PENDING < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((PENDING & 0xF) | (0x7 << 4) | (0x0 << 8) | ((PENDING >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::BN][C::BM],
+                                              int n0, int m0, int wn, int wm, int lane) {
+  // 32x32 accumulator layout: lane l, register r holds column m = l % 32 and row
+  // n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). Per block:
+  // store the int32 sums if asked, dequantize in place to fp32, let the fp16 outlier
+  // MFMA accumulate on top of that, round once to fp16.
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int count = *g.count;
+  const bool overflow = count > g.max_outliers;
+  const int o_pad = min((count + 15) & ~15, g.o_stride);
+  const int M = g.M, N = g.N;
+#pragma unroll
+  for (int i = 0; i < C::BN; ++i) {
+    const int nb = n0 + wn * C::WTN + i * 32;
+    const _Float16* wo_row = g.WoT + static_cast<size_t>(min(nb + l32, N - 1)) * g.o_stride;
+#pragma unroll
+    for (int j = 0; j < C::BM; ++j) {
+      const int m = m0 + wm * C::WTM + j * 32 + l32;
+      const int mc = min(m, M - 1);
+      const float sx = g.a_x[mc] * kInvQMax2;
+      v16f y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + 8 * q + 4 * lhi;
+        const v4f aw = n < N ? *reinterpret_cast<const v4f*>(g.a_w + n) : v4f{};
+        if (g.acc_out && m < M && n < N) {
+          const v4i av = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]};
+          *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(m) * N + n) = av;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[4 * q + e] = static_cast<float>(acc[i][j][4 * q + e]) * sx * aw[e];
+      }
+      const _Float16* xo_row = g.Xo + static_cast<size_t>(mc) * g.o_stride;
+      for (int s = 0; s < o_pad; s += 16) {
+        const v8h fa = *reinterpret_cast<const v8h*>(wo_row + s + 8 * lhi);
+        const v8h fb = *reinterpret_cast<const v8h*>(xo_row + s + 8 * lhi);
+        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
+      }
+      if (m < M) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + 8 * q + 4 * lhi;
+          if (n < N) {
+            v4h out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              out[e] = overflow ? static_cast<_Float16>(__builtin_nanf(""))
+                                : static_cast<_Float16>(y[4 * q + e]);
+            *reinterpret_cast<v4h*>(g.Y + static_cast<size_t>(m) * N + n) = out;
+          }
+        }
+      }
+    }
+  }
+}
+
+// The LDS ring: one __shared__ object per stage, so that the compiler can tell which
+// stage a DMA writes and a fragment read reads (a single array indexed by stage makes
+// it wait for every outstanding DMA before each read).
+template <class C, int S>
+__device__ __forceinline__ char* stage_buf() {
+  __shared__ __attribute__((aligned(1024))) char buf[C::STAGE];
+  return buf;
+}
+
+template <class C>
+struct GemmBlock {
+  const GemmArgs& g;
+  const int8_t* a_src[C::AI];   // per-instruction global chunk addresses at k = 0
+  const int8_t* b_src[C::BI];
+  int a_k[C::AI], b_k[C::BI];   // K offset of this lane's chunk, for the K tail
+  int wave, lane, wn, wm;
+  int rn0, rm0;   // first fragment row of this lane in the A / B tile
+  v16i acc[C::BN][C::BM];
+
+  // Issue the DMA of slab kt into stage S (one 1 KB LDS block per instruction).
+  template <int S>
+  __device__ __forceinline__ void issue(int kt) {
+    const int k0 = kt * C::BK;
+    char* base = stage_buf<C, S>();
+    const int8_t* zero = reinterpret_cast<const int8_t*>(kZero16);
+#pragma unroll
+    for (int i = 0; i < C::AI; ++i)
+      __builtin_amdgcn_global_load_lds(k0 + a_k[i] < g.K ? a_src[i] + k0 : zero,
+                                       I8MM_LDS(base + (i * C::NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::BI; ++i)
+      __builtin_amdgcn_global_load_lds(k0 + b_k[i] < g.K ? b_src[i] + k0 : zero,
+                                       I8MM_LDS(base + C::A_BYTES + (i * C::NW + wave) * 1024),
+                                       16, 0, 0);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void compute() {
+    const char* As = stage_buf<C, S>();
+    const char* Bs = As + C::A_BYTES;
+    const int lhi = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < C::BK / 32; ++s) {
+      const int c = 2 * s + lhi;
+      v4i af[C::BN], bf[C::BM];
+#pragma unroll
+      for (int i = 0; i < C::BN; ++i)
+        af[i] = *reinterpret_cast<const v4i*>(As + lds_off<C::BK>(rn0 + i * 32, c));
+#pragma unroll
+      for (int j = 0; j < C::BM; ++j)
+        bf[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 32, c));
+#pragma unroll
+      for (int i = 0; i < C::BN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::BM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // One K slab: wait for its data (and for every wave to be done with the stage the
+  // next DMA overwrites), refill that stage, multiply. Branch-free: slabs past the
+  // end of K are fetched as zeros, so the wait count never changes.
+  template <int CUR>
+  __device__ __forceinline__ void step(int kt) {
+    constexpr int S = C::STAGES;
+    wait_and_barrier<(S - 2) * (C::AI + C::BI)>();
+    issue<(CUR + S - 1) % S>(kt + S - 1);
+    compute<CUR>();
+  }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int group_m) {
+  GemmBlock<C> b{g};
+  const int tid = threadIdx.x;
+  b.lane = tid & 63;
+  b.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  b.wn = b.wave % C::WGN;
+  b.wm = b.wave / C::WGN;
+  {
+    // The wave's row offsets enter the fragment addresses as per-lane values: folded
+    // in as a scalar they hide which LDS stage a read touches, and the compiler then
+    // waits for every outstanding DMA before each fragment read.
+    const int vw = tid >> 6;
+    b.rn0 = (vw % C::WGN) * C::WTN + (b.lane & 31);
+    b.rm0 = (vw / C::WGN) * C::WTM + (b.lane & 31);
+  }
+  int tn, tm;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, group_m, tn, tm);
+  const int n0 = tn * C::TN, m0 = tm * C::TM;
+  const int K = g.K;
+  // LDS slot p = 64 (i NW + wave) + lane of a tile holds row p / CPR, chunk
+  // (p % CPR) ^ swz(row): fetch that global chunk so the ring holds swizzled tiles.
+#pragma unroll
+  for (int i = 0; i < C::AI; ++i) {
+    const int p = (i * C::NW + b.wave) * 64 + b.lane;
+    const int r = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(r);
+    b.a_src[i] = g.Wq + static_cast<size_t>(min(n0 + r, g.N - 1)) * K + c * 16;
+    b.a_k[i] = c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::BI; ++i) {
+    const int p = (i * C::NW + b.wave) * 64 + b.lane;
+    const int r = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(r);
+    b.b_src[i] = g.Xq + static_cast<size_t>(min(m0 + r, g.M - 1)) * K + c * 16;
+    b.b_k[i] = c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::BN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BM; ++j) b.acc[i][j] = v16i{};
+
+  // K slabs, padded to a multiple of STAGES: the padding slabs read as zeros and add
+  // nothing to the exact int32 sums.
+  const int nk = (K + C::BK - 1) / C::BK;
+  const int nk_pad = (nk + C::STAGES - 1) / C::STAGES * C::STAGES;
+  b.template issue<0>(0);
+  if constexpr (C::STAGES >= 3) b.template issue<1>(1);
+  if constexpr (C::STAGES >= 4) b.template issue<2>(2);
+  for (int kt = 0; kt < nk_pad; kt += C::STAGES) {
+    b.template step<0>(kt);
+    b.template step<1>(kt + 1);
+    if constexpr (C::STAGES >= 3) b.template step<2>(kt + 2);
+    if constexpr (C::STAGES >= 4) b.template step<3>(kt + 3);
+  }
+  // no DMA may still be writing this block's LDS when the block exits
+  __builtin_amdgcn_s_waitcnt(0);
+  gemm_epilogue<C>(g, b.acc, n0, m0, b.wn, b.wm, b.lane);
+}
+
+#undef I8MM_LDS
+
+}  // namespace i8mm

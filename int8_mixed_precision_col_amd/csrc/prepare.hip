@@ -68,10 +68,10 @@ __global__ __launch_bounds__(256) void k_quant_transpose_kn(const _Float16* __re
   const int nl = tid >> 2, kseg = (tid & 3) * 16;
   const int n = n0 + nl, k = k0 + kseg;
   if (n >= N || k >= K) return;
-  const float a = a_w[n];
+  const float a = a_w[n], r = quant_scale(a);
   int q[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) q[e] = quant_code(static_cast<float>(tile[kseg + e][nl]), a);
+  for (int e = 0; e < 16; ++e) q[e] = quant_code_fast(static_cast<float>(tile[kseg + e][nl]), a, r);
   v4u out;
   out[0] = pack4(q[0], q[1], q[2], q[3]);
   out[1] = pack4(q[4], q[5], q[6], q[7]);
@@ -97,13 +97,14 @@ __global__ __launch_bounds__(256) void k_quant_rows_nk(const _Float16* __restric
   }
   m = wave_max(m);
   if (lane == 0) a_w[n] = m;
+  const float r = quant_scale(m);
   for (int c = lane; c < nchunk; c += 64) {
     v8h v = *reinterpret_cast<const v8h*>(row + c * 8);
     v2u o;
-    o[0] = pack4(quant_code(v[0], m), quant_code(v[1], m), quant_code(v[2], m),
-                 quant_code(v[3], m));
-    o[1] = pack4(quant_code(v[4], m), quant_code(v[5], m), quant_code(v[6], m),
-                 quant_code(v[7], m));
+    o[0] = pack4(quant_code_fast(v[0], m, r), quant_code_fast(v[1], m, r),
+                 quant_code_fast(v[2], m, r), quant_code_fast(v[3], m, r));
+    o[1] = pack4(quant_code_fast(v[4], m, r), quant_code_fast(v[5], m, r),
+                 quant_code_fast(v[6], m, r), quant_code_fast(v[7], m, r));
     *reinterpret_cast<v2u*>(Wq + static_cast<size_t>(n) * K + c * 8) = o;
   }
 }

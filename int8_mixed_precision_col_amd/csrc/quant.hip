@@ -67,10 +67,10 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
                                               float* a_x_row, int lane) {
   const int nchunk = K >> 3;
   auto chunk_mask = [&](int c) -> unsigned { return (words[c >> 2] >> ((c & 3) << 3)) & 0xFFu; };
-  auto store_codes = [&](int c, const v8h& v, unsigned mb, float m) {
+  auto store_codes = [&](int c, const v8h& v, unsigned mb, float m, float r) {
     int q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = ((mb >> e) & 1u) ? 0 : quant_code(v[e], m);
+    for (int e = 0; e < 8; ++e) q[e] = ((mb >> e) & 1u) ? 0 : quant_code_fast(v[e], m, r);
     v2u o;
     o[0] = pack4(q[0], q[1], q[2], q[3]);
     o[1] = pack4(q[4], q[5], q[6], q[7]);
@@ -82,7 +82,7 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
-      if (c < nchunk) v[i] = *reinterpret_cast<const v8h*>(xr + c * 8);
+      v[i] = c < nchunk ? *reinterpret_cast<const v8h*>(xr + c * 8) : v8h{};
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -95,10 +95,11 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
       }
     }
     m = wave_max(m);
+    const float r = quant_scale(m);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
-      if (c < nchunk) store_codes(c, v[i], chunk_mask(c), m);
+      if (c < nchunk) store_codes(c, v[i], chunk_mask(c), m, r);
     }
   } else {
     for (int c = lane; c < nchunk; c += 64) {
@@ -109,8 +110,9 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
         if (!((mb >> e) & 1u)) m = fmaxf(m, fabsf(static_cast<float>(v[e])));
     }
     m = wave_max(m);
+    const float r = quant_scale(m);
     for (int c = lane; c < nchunk; c += 64)
-      store_codes(c, *reinterpret_cast<const v8h*>(xr + c * 8), chunk_mask(c), m);
+      store_codes(c, *reinterpret_cast<const v8h*>(xr + c * 8), chunk_mask(c), m, r);
   }
   if (lane == 0) *a_x_row = m;
 }
