@@ -14,7 +14,12 @@
  *
  * Notation: X fp16 [M, K] row-major activations (rows = tokens, columns =
  * feature dimensions). W fp16 weights, K input features x N output features.
- * Wq int8 [N, K] row-major (K contiguous). Codes are symmetric in
+ * Wq: the int8 weight in the "unit-tiled" layout the kernels read: element (n, k)
+ * of the [N, K] matrix is at byte
+ *     ((n / 16) * KS + k / 64) * 1024 + (n % 16) * 64 + k % 64,   KS = ceil(K / 64),
+ * i.e. 16-row x 64-byte units stored contiguously, K-fastest within a group of 16
+ * rows; bytes with k >= K are zero. Size: int8_prepared_weight_bytes(K, N) =
+ * N * KS * 64 bytes. Codes are symmetric in
  * [-127, 127]: q = round-half-even(127 * v / a) for absmax constant a, and
  * q = 0 when a = 0. An outlier column j is one where some row has
  * |X[i, j]| >= threshold.
@@ -65,7 +70,8 @@ typedef enum int8mm_status {
  * per column of the weight matrix).
  *   W         fp16 weights. w_layout 0: [K, N] row-major (x @ W);
  *             w_layout 1: [N, K] row-major (the nn.Linear weight layout).
- *   Wq        out, int8 [N, K] row-major: Wq[n, k] = q(W(k, n), w_absmax[n]).
+ *   Wq        out, int8_prepared_weight_bytes(K, N) bytes, unit-tiled (see the
+ *             notation above): element (n, k) = q(W(k, n), w_absmax[n]).
  *   w_absmax  out, fp32 [N]: max over all K of |W(k, n)| (an exact fp16 value).
  */
 int int8_prepare_weight(const void* W, int64_t K, int64_t N, int w_layout, int8_t* Wq,
@@ -89,6 +95,9 @@ int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t
                     float* x_absmax, uint32_t* outlier_mask, int32_t* outlier_idx,
                     int32_t* n_outliers, int64_t max_outliers, hipStream_t stream);
 
+/* Bytes of a prepared (unit-tiled) int8 weight: N * ceil(K / 64) * 64 (0 on bad shapes). */
+size_t int8_prepared_weight_bytes(int64_t K, int64_t N);
+
 /* Bytes of workspace int8_mixed_matmul needs for this shape (0 on bad arguments). */
 size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers);
 
@@ -99,7 +108,7 @@ size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_
  * into 16-bit floating-point outputs; [Blog] "Mixed-precision
  * decomposition": outlier dimensions in 16 bit, the rest in 8 bit).
  *   X, M, K       fp16 activations [M, K].
- *   Wq, w_absmax  int8 [N, K] and fp32 [N] from int8_prepare_weight.
+ *   Wq, w_absmax  unit-tiled int8 weight and fp32 [N] from int8_prepare_weight.
  *   threshold     outlier threshold, as for int8_quant_rows.
  *   max_outliers  capacity for outlier columns, 0 <= max_outliers <= min(K, 8192). If the
  *                 call finds more, Y is filled with fp16 NaN and the workspace

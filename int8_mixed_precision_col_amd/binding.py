@@ -24,6 +24,7 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "int8_prepare_weight": (_int, [_p, _i64, _i64, _int, _p, _p, _p]),
     "int8_quant_rows": (_int, [_p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _i64, _p]),
+    "int8_prepared_weight_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_mixed_matmul_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
     "int8_mixed_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _f32, _i64, _p, _p,
                                  ctypes.c_size_t, _p, _p]),
@@ -86,14 +87,27 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 
 def prepare_weight(W: torch.Tensor, layout: int = 0):
-    """fp16 W ([K, N] for layout 0, [N, K] for layout 1) -> (Wq int8 [N, K], a_w fp32 [N])."""
+    """fp16 W ([K, N] for layout 0, [N, K] for layout 1) -> (Wq, a_w fp32 [N]).
+
+    Wq is the unit-tiled int8 weight the kernels read (include/int8mm.h): a tensor of
+    shape (N // 16, ceil(K / 64), 16, 64); untile_weight(Wq, K) gives the [N, K] view.
+    """
     _need(W, torch.float16, "W")
     K, N = (W.shape[0], W.shape[1]) if layout == 0 else (W.shape[1], W.shape[0])
-    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    ks = (K + 63) // 64
+    if N % 16:
+        raise ValueError("N must be a multiple of 16")
+    Wq = torch.empty((N // 16, ks, 16, 64), dtype=torch.int8, device=W.device)
     a_w = torch.empty((N,), dtype=torch.float32, device=W.device)
     _check(lib().int8_prepare_weight(W.data_ptr(), K, N, layout, Wq.data_ptr(), a_w.data_ptr(),
                                      _stream(W)), "int8_prepare_weight")
     return Wq, a_w
+
+
+def untile_weight(Wq: torch.Tensor, K: int) -> torch.Tensor:
+    """The [N, K] int8 matrix held in a unit-tiled weight (a copy; layout only)."""
+    g, ks = Wq.shape[0], Wq.shape[1]
+    return Wq.permute(0, 2, 1, 3).reshape(g * 16, ks * 64)[:, :K].contiguous()
 
 
 def quant_rows(X: torch.Tensor, threshold: float, max_outliers: int = 256) -> dict:
@@ -135,15 +149,15 @@ def make_workspace(M: int, K: int, N: int, max_outliers: int = 256, device="cuda
 def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold: float = 6.0,
                  max_outliers: int = 256, workspace: torch.Tensor | None = None,
                  out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None):
-    """Y fp16 [M, N] = the decomposed product of X [M, K] and the prepared weight."""
+    """Y fp16 [M, N] = the decomposed product of X [M, K] and the prepared weight (Wq, a_w)."""
     _need(X, torch.float16, "X")
     _need(Wq, torch.int8, "Wq")
     _need(a_w, torch.float32, "a_w")
     M, K = X.shape
-    N = Wq.shape[0]
-    if Wq.shape[1] != K or a_w.shape[0] != N:
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
-                         f"a_w {tuple(a_w.shape)}")
+    N = a_w.shape[0]
+    if Wq.numel() != int(lib().int8_prepared_weight_bytes(K, N)):
+        raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
+                         f"holds {int(lib().int8_prepared_weight_bytes(K, N))}")
     if workspace is None:
         workspace = make_workspace(M, K, N, max_outliers, X.device)
     _need(workspace, torch.uint8, "workspace")

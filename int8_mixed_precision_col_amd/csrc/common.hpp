@@ -52,6 +52,41 @@ __device__ __forceinline__ unsigned pack4(int a, int b, int c, int d) {
          ((static_cast<unsigned>(c) & 0xFFu) << 16) | (static_cast<unsigned>(d) << 24);
 }
 
+// Codes of 8 halves under absmax a (r = quant_scale(a)); elements whose bit is set in
+// drop (outlier columns) get code 0. Same decision as quant_code_fast, with one
+// near-tie branch per 8 elements instead of one per element.
+__device__ __forceinline__ v2u quant8(const v8h& v, unsigned drop, float a, float r) {
+  float q[8];
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = static_cast<float>(v[e]) * r;
+    q[e] = __builtin_rintf(t);
+    near |= fabsf(t - q[e]) > 0.5f - 0x1p-15f;
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = static_cast<float>(quant_code(v[e], a));
+  }
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = ((drop >> e) & 1u) ? 0 : static_cast<int>(q[e]);
+  v2u o;
+  o[0] = pack4(c[0], c[1], c[2], c[3]);
+  o[1] = pack4(c[4], c[5], c[6], c[7]);
+  return o;
+}
+
+// Block barrier for LDS traffic only: waits for this thread's LDS operations, not for
+// its outstanding global loads (__syncthreads would also drain those). The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -73,6 +108,17 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     if (lane >= o) v += u;
   }
   return v;
+}
+
+// The int8 operand layout of the GEMM and decode kernels ("unit-tiled"): the matrix is
+// cut into units of 16 rows x 64 K-bytes, each stored as 1 KB contiguous (row-major
+// inside), units ordered K-fastest within a 16-row group. KS = ceil(K / 64) units per
+// group; K is zero-padded to 64 * KS. A unit is exactly the 16 x 64 operand of
+// v_mfma_i32_16x16x64_i8, and a 16-row group's whole K extent is contiguous.
+constexpr int kUnitRows = 16, kUnitK = 64, kUnitBytes = kUnitRows * kUnitK;
+__host__ __device__ __forceinline__ int unit_ks(int K) { return (K + kUnitK - 1) / kUnitK; }
+__host__ __device__ __forceinline__ size_t unit_offset(int r, int k, int ks) {
+  return (static_cast<size_t>(r >> 4) * ks + (k >> 6)) * kUnitBytes + (r & 15) * kUnitK + (k & 63);
 }
 
 // Raw buffer resource over [base, base + bytes). Loads whose offset lies outside

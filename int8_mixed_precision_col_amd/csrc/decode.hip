@@ -72,20 +72,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
-  const int nsteps = (K + 63) / 64;
-  const int kl = 16 * (lane >> 4);
 
-  // 1. the weight stream: wave w takes k-steps w, w + 4, ...
-  v4i wf[SPW];
-  const int8_t* wrow = a.Wq + static_cast<size_t>(n0 + (lane & 15)) * K + kl;
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int step = wave + 4 * i;
-    wf[i] = (step < nsteps && 64 * step + kl < K) ? *reinterpret_cast<const v4i*>(wrow + 64 * step)
-                                                  : v4i{};
-  }
-
-  // 2. activations into registers
+  // 1. activations into registers (loaded first: the vmcnt wait for them then leaves
+  // every weight load in flight)
   v8h xv[RW][CL];
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
@@ -93,13 +82,37 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < CL; ++j) {
       const int c = lane + 64 * j;
-      xv[i][j] = (m < M && c < nchunk)
-                     ? *reinterpret_cast<const v8h*>(a.X + static_cast<size_t>(m) * K + c * 8)
-                     : v8h{};
+      const v8h v = *reinterpret_cast<const v8h*>(a.X + static_cast<size_t>(min(m, M - 1)) * K +
+                                                  min(c, nchunk - 1) * 8);
+      xv[i][j] = (m < M && c < nchunk) ? v : v8h{};
     }
   }
+  // 2. the weight stream. Wq is unit-tiled: the block's 16 rows are one contiguous
+  // run of KS units, and unit s is exactly the 16 x 64 A operand of k-step s, so each
+  // load instruction reads one whole 1 KB unit. Wave w takes steps w, w + 4, ...; each
+  // block starts at a different step so that concurrent blocks spread over HBM
+  // channels instead of all hitting the same offsets. The K padding holds zeros.
+  const int ks = unit_ks(K);
+  const int nsteps = ks;
+  const int kl = 16 * (lane >> 4);
+  v4i wf[SPW];
+  int wstep[SPW];
+  const int8_t* wunit = a.Wq + static_cast<size_t>(n0 >> 4) * ks * kUnitBytes + (lane & 15) * kUnitK + kl;
+  const int nmine = (nsteps - wave + 3) / 4;  // steps of this wave
+  const int rot = nmine > 0 ? static_cast<int>(blockIdx.x * 5u % static_cast<unsigned>(nmine)) : 0;
+  // Loads are unconditional (a guarded load becomes a branch whose join waits for the
+  // data): slots past this wave's share re-read unit 0 and are skipped by the MFMA.
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    int j = i + rot;
+    j = j >= nmine ? j - nmine : j;
+    const int step = i < nmine ? wave + 4 * j : 0;
+    wstep[i] = i < nmine ? step : -1;
+    wf[i] = *reinterpret_cast<const v4i*>(wunit + static_cast<size_t>(step) * kUnitBytes);
+  }
+
   for (int w = tid; w < W; w += 256) mask_s[w] = 0;
-  __syncthreads();
+  lds_barrier();
 
   // outlier flags of this wave's rows, per owned chunk (OR over rows), into LDS
 #pragma unroll
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       atomicOr(&mask_s[c >> 2], f << ((c & 3) << 3));
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3. rank outlier columns (thread t owns words [t*per, (t+1)*per))
   const int per = (W + 255) / 256;
@@ -160,18 +173,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     for (int j = 0; j < CL; ++j) {
       const int c = lane + 64 * j;
       if (c < nchunk) {
-        int q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          q[e] = ((mbyte[j] >> e) & 1u) ? 0 : quant_code_fast(xv[i][j][e], am, r);
-        v2u o;
-        o[0] = pack4(q[0], q[1], q[2], q[3]);
-        o[1] = pack4(q[4], q[5], q[6], q[7]);
+        const v2u o = quant8(xv[i][j], mbyte[j], am, r);
         *reinterpret_cast<v2u*>(xq_s + m * xs + c * 8) = o;
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   int before = incl - mine;
   for (int i = 0; i < wave; ++i) before += wave_tot[i];
   const int count = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
@@ -189,9 +196,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   const int mtok = lane & 15;
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int step = wave + 4 * i;
-    if (step < nsteps) {
-      const int k = 64 * step + kl;
+    if (wstep[i] >= 0) {  // wave-uniform
+      const int k = 64 * wstep[i] + kl;
       const v4i xf = (mtok < M && k < K) ? *reinterpret_cast<const v4i*>(xq_s + mtok * xs + k)
                                          : v4i{};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], xf, acc, 0, 0, 0);
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   // 16x16 accumulator layout: lane l, register r -> column m = l % 16, row 4 (l / 16) + r
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][mtok] = acc[r];
-  __syncthreads();
+  lds_barrier();
 
   // 5. epilogue: thread -> (token m, output feature n0 + nl)
   const int m = tid >> 4, nl = tid & 15, n = n0 + nl;
@@ -210,12 +216,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     for (int t = tid; t < rn * 16; t += 256) {
       const int r = t >> 4, q = t & 15;
       const int col = idx_s[r0 + r];
-      wo_s[r * 16 + q] = static_cast<float>(a.Wq[static_cast<size_t>(n0 + q) * K + col]);
+      wo_s[r * 16 + q] = static_cast<float>(a.Wq[unit_offset(n0 + q, col, ks)]);
       xo_s[r * 16 + q] = q < M ? static_cast<float>(a.X[static_cast<size_t>(q) * K + col]) : 0.0f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int r = 0; r < rn; ++r) yo += xo_s[r * 16 + m] * wo_s[r * 16 + nl];
-    __syncthreads();
+    lds_barrier();
   }
   const bool overflow = count > a.max_outliers;
   if (m < M) {

@@ -3,8 +3,10 @@
 
 namespace i8mm {
 
-using CfgL = GemmCfg<256, 256, 64, 2, 2, 3>;  // large problems
-using CfgS = GemmCfg<128, 128, 64, 2, 2, 3>;  // small or skinny problems
+// Large problems: 256 x 256 tiles, 8 waves (two per SIMD, 128 x 64 each), 3-stage ring.
+using CfgL = GemmCfg<256, 256, 64, 2, 4, 3>;
+// Small or skinny problems: 128 x 128 tiles, 4 waves.
+using CfgS = GemmCfg<128, 128, 64, 2, 2, 3>;
 
 template <class C>
 static hipError_t run(const GemmArgs& g, hipStream_t s, int group_m) {

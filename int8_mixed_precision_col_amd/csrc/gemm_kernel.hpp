@@ -16,11 +16,13 @@
 // A block of WGN x WGM waves owns a TN x TM tile; each wave a (TN/WGN) x (TM/WGM)
 // sub-tile of 32x32 blocks whose int32 accumulators live in registers.
 // K is walked in BK-byte slabs through a ring of STAGES LDS buffers filled by
-// global_load_lds_dwordx4 (global memory straight into LDS, no VGPR staging): rows
-// past the tile edge are clamped to the last row (their outputs are discarded),
-// chunks past the end of K read a 16-byte zero constant, and each lane fetches the
-// global 16-byte chunk that belongs at its LDS slot under an XOR swizzle, so that the
-// ds_read_b128 fragment reads are free of bank conflicts. Slab kt + STAGES - 1 is in
+// global_load_lds_dwordx4 (global memory straight into LDS, no VGPR staging) from
+// unit-tiled operands (16 rows x 64 K-bytes per contiguous 1 KB unit), so that each
+// DMA instruction reads whole cache lines: rows past the tile edge are clamped to the
+// last row (their outputs are discarded), the K padding holds zeros and slabs past it
+// read a 16-byte zero constant, and each lane fetches the global 16-byte chunk that
+// belongs at its LDS slot under an XOR swizzle, so that the ds_read_b128 fragment
+// reads are free of bank conflicts. Slab kt + STAGES - 1 is in
 // flight while slab kt is multiplied; one barrier per slab.
 // The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, reading the
 // small Xo / WoT fragments straight from global memory (L2-resident), accumulating
@@ -32,9 +34,11 @@
 
 namespace i8mm {
 
-template <int TN_, int TM_, int BK_, int WGN_, int WGM_, int STAGES_>
+// CPOL: cache-policy bits of the DMA loads (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
+template <int TN_, int TM_, int BK_, int WGN_, int WGM_, int STAGES_, int CPOL_ = 0>
 struct GemmCfg {
   static constexpr int TN = TN_, TM = TM_, BK = BK_, WGN = WGN_, WGM = WGM_, STAGES = STAGES_;
+  static constexpr int CPOL = CPOL_;
   static constexpr int NW = WGN * WGM, NT = NW * 64;
   static constexpr int WTN = TN / WGN, WTM = TM / WGM;
   static constexpr int BN = WTN / 32, BM = WTM / 32;
@@ -44,7 +48,7 @@ struct GemmCfg {
   static constexpr int AI = A_BYTES / (1024 * NW);    // 1 KB DMA instructions per wave, A
   static constexpr int BI = B_BYTES / (1024 * NW);    // ... and B
   static_assert(AI * 1024 * NW == A_BYTES && BI * 1024 * NW == B_BYTES, "tile / wave mismatch");
-  static_assert(BK % 32 == 0 && WTN % 32 == 0 && WTM % 32 == 0, "shape");
+  static_assert(BK % 64 == 0 && WTN % 32 == 0 && WTM % 32 == 0, "shape");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
 };
 
@@ -84,12 +88,27 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int g
 
 #define I8MM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// One 16-byte-per-lane DMA from global memory into LDS (base + 16 * lane). The cache
+// policy must reach the builtin as a literal.
+template <int CPOL>
+__device__ __forceinline__ void dma16(const void* src, __attribute__((address_space(3))) void* dst) {
+  if constexpr (CPOL == 1) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 1);
+  else if constexpr (CPOL == 2) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+  else if constexpr (CPOL == 3) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 3);
+  else __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 // Source of the K-tail chunks: multiplying by zeros adds nothing to the int32 sums.
 __device__ __attribute__((aligned(16))) const int kZero16[4] = {0, 0, 0, 0};
 
 // Waits until at most `pending` of this thread's buffer loads are outstanding and all
 // its LDS reads are done, then joins the block barrier. The empty asm statements keep
 // the compiler from moving memory accesses across the barrier.
+// Waits for this thread's outstanding LDS reads only (vmcnt and expcnt left open).
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 template <int PENDING>
 __device__ __forceinline__ void wait_and_barrier() {
   static_assert(PENDING >= 0 && PENDING < 64, "vmcnt range");
@@ -171,62 +190,91 @@ __device__ __forceinline__ char* stage_buf() {
 template <class C>
 struct GemmBlock {
   const GemmArgs& g;
-  const int8_t* a_src[C::AI];   // per-instruction global chunk addresses at k = 0
+  const int8_t* a_src[C::AI];   // per-instruction global chunk addresses of slab 0
   const int8_t* b_src[C::BI];
-  int a_k[C::AI], b_k[C::BI];   // K offset of this lane's chunk, for the K tail
+  int a_k[C::AI], b_k[C::BI];   // K offset of this lane's chunk within a slab
   int wave, lane, wn, wm;
   int rn0, rm0;   // first fragment row of this lane in the A / B tile
   v16i acc[C::BN][C::BM];
 
   // Issue the DMA of slab kt into stage S (one 1 KB LDS block per instruction).
+  // Slab kt starts kt * BK / 64 units further along each row group.
   template <int S>
   __device__ __forceinline__ void issue(int kt) {
     const int k0 = kt * C::BK;
+    const size_t step = static_cast<size_t>(kt) * (C::BK / kUnitK) * kUnitBytes;
+    const int kpad = unit_ks(g.K) * kUnitK;
     char* base = stage_buf<C, S>();
     const int8_t* zero = reinterpret_cast<const int8_t*>(kZero16);
 #pragma unroll
     for (int i = 0; i < C::AI; ++i)
-      __builtin_amdgcn_global_load_lds(k0 + a_k[i] < g.K ? a_src[i] + k0 : zero,
-                                       I8MM_LDS(base + (i * C::NW + wave) * 1024), 16, 0, 0);
+      dma16<C::CPOL>(k0 + a_k[i] < kpad ? a_src[i] + step : zero,
+                     I8MM_LDS(base + (i * C::NW + wave) * 1024));
 #pragma unroll
     for (int i = 0; i < C::BI; ++i)
-      __builtin_amdgcn_global_load_lds(k0 + b_k[i] < g.K ? b_src[i] + k0 : zero,
-                                       I8MM_LDS(base + C::A_BYTES + (i * C::NW + wave) * 1024),
-                                       16, 0, 0);
+      dma16<C::CPOL>(k0 + b_k[i] < kpad ? b_src[i] + step : zero,
+                     I8MM_LDS(base + C::A_BYTES + (i * C::NW + wave) * 1024));
   }
 
+  struct Frags {
+    v4i a[C::BN], b[C::BM];
+  };
+
+  // Fragments of substep s (32 K bytes) of the slab held in stage S.
   template <int S>
-  __device__ __forceinline__ void compute() {
+  __device__ __forceinline__ void load_frags(Frags& f, int s) const {
     const char* As = stage_buf<C, S>();
     const char* Bs = As + C::A_BYTES;
-    const int lhi = lane >> 5;
+    const int c = 2 * s + (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < C::BK / 32; ++s) {
-      const int c = 2 * s + lhi;
-      v4i af[C::BN], bf[C::BM];
+    for (int i = 0; i < C::BN; ++i)
+      f.a[i] = *reinterpret_cast<const v4i*>(As + lds_off<C::BK>(rn0 + i * 32, c));
 #pragma unroll
-      for (int i = 0; i < C::BN; ++i)
-        af[i] = *reinterpret_cast<const v4i*>(As + lds_off<C::BK>(rn0 + i * 32, c));
-#pragma unroll
-      for (int j = 0; j < C::BM; ++j)
-        bf[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 32, c));
-#pragma unroll
-      for (int i = 0; i < C::BN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::BM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < C::BM; ++j)
+      f.b[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 32, c));
   }
 
-  // One K slab: wait for its data (and for every wave to be done with the stage the
-  // next DMA overwrites), refill that stage, multiply. Branch-free: slabs past the
-  // end of K are fetched as zeros, so the wait count never changes.
+  __device__ __forceinline__ void mma(const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < C::BN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::BM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  }
+
+  // One K slab held in stage CUR, whose first-substep fragments are already in f.
+  // Substep s + 1's fragments are read while substep s multiplies. Before the last
+  // substep (whose fragments are in registers by then): wait until slab kt + 1 has
+  // landed (this thread's DMA, then the barrier for everyone else's; the slabs up to
+  // kt + STAGES - 1 may still be in flight), refill stage CUR - free now that every
+  // wave has read all of slab kt - with slab kt + STAGES, and read slab kt + 1's first
+  // fragments while the last MFMAs of slab kt run.
   template <int CUR>
-  __device__ __forceinline__ void step(int kt) {
-    constexpr int S = C::STAGES;
+  __device__ __forceinline__ void step(int kt, Frags& f) {
+    constexpr int S = C::STAGES, NS = C::BK / 32;
+    Frags nxt;
+    // sched_barrier(0) keeps the compiler from sinking the fragment reads down to
+    // their MFMAs, which would expose the LDS latency once per substep. The explicit
+    // LDS-read drain before each read batch (whose targets were read a whole MFMA
+    // block earlier, so it costs nothing) lets the MFMAs run without a wait: with DMA
+    // in flight the compiler would otherwise wait for every LDS read, the batch just
+    // issued included, before the first MFMA.
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s) {
+      lds_reads_done();
+      load_frags<CUR>(nxt, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f);
+      __builtin_amdgcn_sched_barrier(0);
+      f = nxt;
+    }
     wait_and_barrier<(S - 2) * (C::AI + C::BI)>();
-    issue<(CUR + S - 1) % S>(kt + S - 1);
-    compute<CUR>();
+    issue<CUR>(kt + S);
+    load_frags<(CUR + 1) % S>(nxt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f);
+    __builtin_amdgcn_sched_barrier(0);
+    f = nxt;
   }
 };
 
@@ -252,18 +300,23 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
   const int K = g.K;
   // LDS slot p = 64 (i NW + wave) + lane of a tile holds row p / CPR, chunk
   // (p % CPR) ^ swz(row): fetch that global chunk so the ring holds swizzled tiles.
+  // The operands are unit-tiled (common.hpp), so every 1 KB DMA instruction reads
+  // whole 64-byte unit rows (BK = 64: one contiguous unit). Rows past the edge are
+  // clamped to the last row (their outputs are discarded); Xq rows are padded to 16.
+  const int ks = unit_ks(K);
+  const int m_rows = (g.M + 15) & ~15;
 #pragma unroll
   for (int i = 0; i < C::AI; ++i) {
     const int p = (i * C::NW + b.wave) * 64 + b.lane;
     const int r = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(r);
-    b.a_src[i] = g.Wq + static_cast<size_t>(min(n0 + r, g.N - 1)) * K + c * 16;
+    b.a_src[i] = g.Wq + unit_offset(min(n0 + r, g.N - 1), c * 16, ks);
     b.a_k[i] = c * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::BI; ++i) {
     const int p = (i * C::NW + b.wave) * 64 + b.lane;
     const int r = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(r);
-    b.b_src[i] = g.Xq + static_cast<size_t>(min(m0 + r, g.M - 1)) * K + c * 16;
+    b.b_src[i] = g.Xq + unit_offset(min(m0 + r, m_rows - 1), c * 16, ks);
     b.b_k[i] = c * 16;
   }
 #pragma unroll
@@ -273,16 +326,20 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
 
   // K slabs, padded to a multiple of STAGES: the padding slabs read as zeros and add
   // nothing to the exact int32 sums.
-  const int nk = (K + C::BK - 1) / C::BK;
+  const int nk = (ks * kUnitK + C::BK - 1) / C::BK;
   const int nk_pad = (nk + C::STAGES - 1) / C::STAGES * C::STAGES;
   b.template issue<0>(0);
-  if constexpr (C::STAGES >= 3) b.template issue<1>(1);
-  if constexpr (C::STAGES >= 4) b.template issue<2>(2);
+  b.template issue<1>(1);
+  if constexpr (C::STAGES >= 3) b.template issue<2>(2);
+  if constexpr (C::STAGES >= 4) b.template issue<3>(3);
+  typename GemmBlock<C>::Frags f;
+  wait_and_barrier<(C::STAGES - 1) * (C::AI + C::BI)>();   // slab 0 landed
+  b.template load_frags<0>(f, 0);
   for (int kt = 0; kt < nk_pad; kt += C::STAGES) {
-    b.template step<0>(kt);
-    b.template step<1>(kt + 1);
-    if constexpr (C::STAGES >= 3) b.template step<2>(kt + 2);
-    if constexpr (C::STAGES >= 4) b.template step<3>(kt + 3);
+    b.template step<0>(kt, f);
+    b.template step<1>(kt + 1, f);
+    if constexpr (C::STAGES >= 3) b.template step<2>(kt + 2, f);
+    if constexpr (C::STAGES >= 4) b.template step<3>(kt + 3, f);
   }
   // no DMA may still be writing this block's LDS when the block exits
   __builtin_amdgcn_s_waitcnt(0);

@@ -6,6 +6,7 @@
 #include <utility>
 #include <vector>
 
+#include "common.hpp"
 #include "int8mm.h"
 #include "launch.hpp"
 
@@ -41,7 +42,7 @@ struct Layout {
 };
 
 // Workspace: [status, count] header, then (prefill only) the row-chunk column flags,
-// a_x, Xq, Xo and WoT, each 256-byte aligned.
+// a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and WoT, each 256-byte aligned.
 Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   Layout L;
   size_t off = 256;
@@ -50,11 +51,12 @@ Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
     return L;
   }
   const size_t W = (K + 31) / 32;
+  const size_t m_rows = (M + 15) & ~int64_t(15);
   L.R = mask_row_chunks(M, K);
   L.o_stride = static_cast<int>((max_outliers + 15) & ~int64_t(15));
   L.partial = off; off += round256(size_t(L.R) * W * 4);
   L.a_x = off;     off += round256(size_t(M) * 4);
-  L.xq = off;      off += round256(size_t(M) * K);
+  L.xq = off;      off += round256(m_rows * i8mm::unit_ks(int(K)) * i8mm::kUnitK);
   L.xo = off;      off += round256(size_t(M) * L.o_stride * 2);
   L.wot = off;     off += round256(size_t(N) * L.o_stride * 2);
   L.total = off;
@@ -115,11 +117,16 @@ int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t
   i8mm::QuantRowsArgs q{};
   q.X = x; q.M = int(M); q.K = int(K);
   q.partial = outlier_mask; q.R = 1;
-  q.Xq = Xq; q.a_x = x_absmax;
+  q.Xq = Xq; q.xq_tiled = 0; q.a_x = x_absmax;
   q.idx_out = max_outliers > 0 ? outlier_idx : nullptr;
   q.count_out = n_outliers; q.status_out = nullptr;
   q.max_outliers = int(max_outliers);
   return hip_status(i8mm::launch_quant_rows(q, stream));
+}
+
+size_t int8_prepared_weight_bytes(int64_t K, int64_t N) {
+  if (bad_k(K) || bad_n(N)) return 0;
+  return static_cast<size_t>(N) * i8mm::unit_ks(int(K)) * i8mm::kUnitK;
 }
 
 size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
@@ -172,7 +179,7 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   i8mm::QuantRowsArgs q{};
   q.X = x; q.M = int(M); q.K = int(K);
   q.partial = partial; q.R = L.R;
-  q.Xq = xq; q.a_x = a_x;
+  q.Xq = xq; q.xq_tiled = 1; q.a_x = a_x;
   q.idx_out = nullptr; q.count_out = status + 1; q.status_out = status;
   q.max_outliers = int(max_outliers);
   q.Xo = xo; q.o_stride = L.o_stride;

@@ -7,7 +7,7 @@
 
 namespace i8mm {
 
-// Weight conversion: W fp16 [K, N] (layout 0) or [N, K] (layout 1) -> Wq [N, K], a_w [N].
+// Weight conversion: W fp16 [K, N] (layout 0) or [N, K] (layout 1) -> unit-tiled Wq, a_w [N].
 hipError_t launch_prepare_weight(const _Float16* W, int K, int N, int layout, int8_t* Wq,
                                  float* a_w, hipStream_t s);
 
@@ -21,6 +21,7 @@ struct QuantRowsArgs {
   const uint32_t* partial;  // [R][W] column flags from launch_outlier_mask
   int R;
   int8_t* Xq;
+  int xq_tiled;         // 0: Xq row-major [M][K]; 1: unit-tiled (GEMM operand layout)
   float* a_x;
   int32_t* idx_out;     // [max_outliers], nullable when max_outliers == 0
   int32_t* count_out;   // [1]
@@ -28,7 +29,7 @@ struct QuantRowsArgs {
   int max_outliers;
   _Float16* Xo;         // nullable: [M][o_stride] fp16 outlier activations
   int o_stride;         // multiple of 16, >= max_outliers
-  const int8_t* Wq;     // for the WoT gather (nullable = no gather)
+  const int8_t* Wq;     // unit-tiled, for the WoT gather (nullable = no gather)
   const float* a_w;
   int N;
   _Float16* WoT;        // [N][o_stride] fp16 dequantized outlier weight rows
@@ -36,8 +37,8 @@ struct QuantRowsArgs {
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
 
 struct GemmArgs {
-  const int8_t* Wq;   // [N][K]
-  const int8_t* Xq;   // [M][K]
+  const int8_t* Wq;   // unit-tiled [N][K]
+  const int8_t* Xq;   // unit-tiled [M][K] (rows padded to a multiple of 16)
   int M, N, K;
   const float* a_x;
   const float* a_w;
@@ -55,7 +56,7 @@ struct DecodeArgs {
   const _Float16* X;  // [M][K]
   int M, K;
   float t;
-  const int8_t* Wq;   // [N][K]
+  const int8_t* Wq;   // unit-tiled [N][K]
   const float* a_w;
   int N;
   int max_outliers;

@@ -1,4 +1,4 @@
-// Weight conversion: fp16 W -> int8 Wq [N, K] (K contiguous) + fp32 column absmax.
+// Weight conversion: fp16 W -> int8 Wq (unit-tiled, see common.hpp) + fp32 column absmax.
 //
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", Abstract: a
 // 16/32-bit checkpoint is converted to Int8 when it is loaded. "Compress your LLMs",
@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void k_colmax_kn(const _Float16* __restrict__ 
   }
 }
 
-// Wq[n, k] = q(W[k, n], a_w[n]) for a 64 (k) x 64 (n) tile, transposed through LDS.
+// Wq(n, k) = q(W[k, n], a_w[n]) for a 64 (k) x 64 (n) tile, transposed through LDS;
+// K-padding bytes (k >= K in the last unit) are written as zero codes.
 __global__ __launch_bounds__(256) void k_quant_transpose_kn(const _Float16* __restrict__ W, int K,
                                                             int N, const float* __restrict__ a_w,
                                                             int8_t* __restrict__ Wq) {
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void k_quant_transpose_kn(const _Float16* __re
   // store: thread -> (n row, 16 consecutive k)
   const int nl = tid >> 2, kseg = (tid & 3) * 16;
   const int n = n0 + nl, k = k0 + kseg;
-  if (n >= N || k >= K) return;
+  if (n >= N) return;  // k < 64 * unit_ks(K): loaded as zeros past K, so codes are 0
   const float a = a_w[n], r = quant_scale(a);
   int q[16];
 #pragma unroll
@@ -77,10 +78,11 @@ __global__ __launch_bounds__(256) void k_quant_transpose_kn(const _Float16* __re
   out[1] = pack4(q[4], q[5], q[6], q[7]);
   out[2] = pack4(q[8], q[9], q[10], q[11]);
   out[3] = pack4(q[12], q[13], q[14], q[15]);
-  *reinterpret_cast<v4u*>(Wq + static_cast<size_t>(n) * K + k) = out;
+  *reinterpret_cast<v4u*>(Wq + unit_offset(n, k, unit_ks(K))) = out;
 }
 
-// W [N, K] row-major (output-feature rows): one wave per row, absmax then quantize.
+// W [N, K] row-major (output-feature rows): one wave per row, absmax then quantize;
+// the row's K padding is written as zero codes.
 __global__ __launch_bounds__(256) void k_quant_rows_nk(const _Float16* __restrict__ W, int K, int N,
                                                        int8_t* __restrict__ Wq,
                                                        float* __restrict__ a_w) {
@@ -105,8 +107,11 @@ __global__ __launch_bounds__(256) void k_quant_rows_nk(const _Float16* __restric
                  quant_code_fast(v[2], m, r), quant_code_fast(v[3], m, r));
     o[1] = pack4(quant_code_fast(v[4], m, r), quant_code_fast(v[5], m, r),
                  quant_code_fast(v[6], m, r), quant_code_fast(v[7], m, r));
-    *reinterpret_cast<v2u*>(Wq + static_cast<size_t>(n) * K + c * 8) = o;
+    *reinterpret_cast<v2u*>(Wq + unit_offset(n, c * 8, unit_ks(K))) = o;
   }
+  const int ks = unit_ks(K);
+  for (int c = nchunk + lane; c < ks * 8; c += 64)
+    *reinterpret_cast<v2u*>(Wq + unit_offset(n, c * 8, ks)) = v2u{0u, 0u};
 }
 
 hipError_t launch_prepare_weight(const _Float16* W, int K, int N, int layout, int8_t* Wq,

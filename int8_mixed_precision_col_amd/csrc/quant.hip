@@ -14,8 +14,9 @@
 //                   atomics and no pre-zeroed memory: every word is written).
 //   k_quant_rows    ORs the chunk flags, ranks the outlier columns with a block scan,
 //                   then one wave per row: absmax over kept columns, quantize, store
-//                   Xq; gathers the fp16 outlier activations Xo. Extra blocks gather
-//                   the dequantized int8 weight rows of the outlier columns, WoT.
+//                   Xq (row-major, or unit-tiled for the GEMM); gathers the fp16
+//                   outlier activations Xo. Extra blocks gather the dequantized int8
+//                   weight rows of the outlier columns, WoT.
 // Both are HBM-bound streaming kernels (X read, Xq written).
 #include "common.hpp"
 #include "launch.hpp"
@@ -61,20 +62,19 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
 
 // One wave quantizes one row. CH > 0: the row is held in registers (CH chunks of 8
 // halves per lane, K <= 512 * CH) and read once; CH == 0: streamed twice.
+// Xq goes row-major (ks == 0) or unit-tiled with ks = unit_ks(K) units per row group,
+// in which case the row's K padding is written as zero codes.
 template <int CH>
 __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, int K,
-                                              const uint32_t* words, int8_t* __restrict__ xq,
-                                              float* a_x_row, int lane) {
+                                              const uint32_t* words, int8_t* __restrict__ Xq,
+                                              int row, int ks, float* a_x_row, int lane) {
   const int nchunk = K >> 3;
+  auto dst = [&](int c) -> int8_t* {
+    return ks ? Xq + unit_offset(row, c * 8, ks) : Xq + static_cast<size_t>(row) * K + c * 8;
+  };
   auto chunk_mask = [&](int c) -> unsigned { return (words[c >> 2] >> ((c & 3) << 3)) & 0xFFu; };
   auto store_codes = [&](int c, const v8h& v, unsigned mb, float m, float r) {
-    int q[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = ((mb >> e) & 1u) ? 0 : quant_code_fast(v[e], m, r);
-    v2u o;
-    o[0] = pack4(q[0], q[1], q[2], q[3]);
-    o[1] = pack4(q[4], q[5], q[6], q[7]);
-    *reinterpret_cast<v2u*>(xq + c * 8) = o;
+    *reinterpret_cast<v2u*>(dst(c)) = quant8(v, mb, m, r);
   };
   float m = 0.0f;
   if constexpr (CH > 0) {
@@ -115,6 +115,8 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
       store_codes(c, *reinterpret_cast<const v8h*>(xr + c * 8), chunk_mask(c), m, r);
   }
   if (lane == 0) *a_x_row = m;
+  if (ks)
+    for (int c = nchunk + lane; c < ks * 8; c += 64) *reinterpret_cast<v2u*>(dst(c)) = v2u{0u, 0u};
 }
 
 // Blocks [0, nrow): rows 4b..4b+3 (one wave each). Blocks [nrow, nrow + ngather): WoT
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
     const int row = blockIdx.x * 4 + wave;
     if (row >= a.M) return;
     const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
-    quant_one_row<CH>(xr, a.K, words, a.Xq + static_cast<size_t>(row) * a.K, a.a_x + row, lane);
+    quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane);
     if (a.Xo) {
       _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
       for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
     const int n = (blockIdx.x - nrow) * 256 + tid;
     if (n >= a.N) return;
     const float aw = a.a_w[n];
-    const int8_t* wr = a.Wq + static_cast<size_t>(n) * a.K;
+    const int ks = unit_ks(a.K);
     _Float16* dst = a.WoT + static_cast<size_t>(n) * a.o_stride;
     for (int r0 = 0; r0 < o_pad; r0 += 8) {
       v8h o;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
       for (int e = 0; e < 8; ++e) {
         const int r = r0 + e;
         o[e] = r < count ? static_cast<_Float16>(
-                               __fdiv_rn(static_cast<float>(wr[idx_s[r]]) * aw, 127.0f))
+                               __fdiv_rn(static_cast<float>(a.Wq[unit_offset(n, idx_s[r], ks)]) * aw, 127.0f))
                          : _Float16(0);
       }
       *reinterpret_cast<v8h*>(dst + r0) = o;

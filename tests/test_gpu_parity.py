@@ -32,7 +32,7 @@ def weight(seed, K, N, std=0.02):
 # ------------------------------------------------------------------ prepare
 
 @pytest.mark.parametrize("K,N,layout", [(1024, 1024, 0), (1040, 528, 0), (1040, 528, 1),
-                                        (16, 16, 0), (4112, 80, 1)])
+                                        (16, 16, 0), (4112, 80, 1), (48, 32, 0), (48, 32, 1)])
 def test_prepare_weight_bit_exact(K, N, layout):
     announce(f"prepare_weight K={K} N={N} layout={layout}")
     W = weight(K + N, K, N)
@@ -41,7 +41,10 @@ def test_prepare_weight_bit_exact(K, N, layout):
     src = W if layout == 0 else np.ascontiguousarray(W.T)
     Wq, aw = binding.prepare_weight(dev(src), layout)
     assert np.array_equal(host(aw), aw_ref)
-    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(binding.untile_weight(Wq, K)), Wq_ref)
+    # the K padding of the last unit holds zero codes
+    pad = host(Wq).reshape(N // 16, -1, 16, 64)[:, -1, :, K % 64:] if K % 64 else None
+    assert pad is None or not pad.any()
 
 
 # ------------------------------------------------------------------ quant rows
