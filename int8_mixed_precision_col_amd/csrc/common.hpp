@@ -77,6 +77,117 @@ __device__ __forceinline__ v2u quant8(const v8h& v, unsigned drop, float a, floa
   return o;
 }
 
+// fp32 1.5 * 2^23. For |p| < 2^22, the fused fma(x, r, kRoundMagic) rounds the exact
+// product p = x r to an integer (half-even, in the adder) and leaves that integer, as
+// kRoundMagic + q, in the result's low bits: its low byte is q as an int8.
+constexpr float kRoundMagic = 12582912.0f;
+
+// The two fp32 neighbours of RN(127 / a), which bracket the exact 127 / a; both 0 for
+// a == 0. For a finite a > 0, RN(127 / a) is a normal float and so are its neighbours.
+struct QuantBracket {
+  float lo, hi;
+};
+__device__ __forceinline__ QuantBracket quant_bracket(float a) {
+  if (a == 0.0f) return {0.0f, 0.0f};
+  const unsigned r = __builtin_bit_cast(unsigned, __fdiv_rn(127.0f, a));
+  return {__builtin_bit_cast(float, r - 1u), __builtin_bit_cast(float, r + 1u)};
+}
+
+// Low bytes of four dwords, packed little-endian (v_perm_b32 selects bytes of {S0, S1}:
+// selector 0-3 takes S1's bytes, 4-7 S0's, 0x0c gives 0).
+__device__ __forceinline__ unsigned pack_low_bytes(unsigned b0, unsigned b1, unsigned b2,
+                                                   unsigned b3) {
+  const unsigned lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const unsigned hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Codes of 8 halves under absmax a, with br = quant_bracket(a): quant_code of each.
+// p_lo = x br.lo and p_hi = x br.hi bracket the exact 127 x / a, and round-half-even
+// is monotonic, so where both round to the same integer that integer is the exact
+// code; only 8-element groups holding a disagreement (a value within about 2^-15 of a
+// half-integer) take the correctly rounded divide.
+__device__ __forceinline__ v2u quant8_bracket(const v8h& x, float a, QuantBracket br) {
+  unsigned b1[8], b2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = static_cast<float>(x[e]);
+    b1[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.lo, kRoundMagic));
+    b2[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.hi, kRoundMagic));
+  }
+  v2u o;
+  o[0] = pack_low_bytes(b1[0], b1[1], b1[2], b1[3]);
+  o[1] = pack_low_bytes(b1[4], b1[5], b1[6], b1[7]);
+  const unsigned d0 = o[0] ^ pack_low_bytes(b2[0], b2[1], b2[2], b2[3]);
+  const unsigned d1 = o[1] ^ pack_low_bytes(b2[4], b2[5], b2[6], b2[7]);
+  if (__builtin_expect((d0 | d1) != 0u, 0)) {
+    int c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = quant_code(static_cast<float>(x[e]), a);
+    o[0] = pack4(c[0], c[1], c[2], c[3]);
+    o[1] = pack4(c[4], c[5], c[6], c[7]);
+  }
+  return o;
+}
+
+// Exact codes of 8 halves under absmax a, for groups where the quant8_bracket pair
+// disagreed. With w = |x| and q1 = RNE(w * lo) (lo = quant_bracket(a).lo <= 127 / a),
+// the code of w is q1 or q1 + 1; it is q1 + 1 exactly when 127 w / a > q1 + 1/2, or
+// equals it with q1 odd (half-even). That comparison, 254 w against (2 q1 + 1) a, is
+// made exactly: 254 w and (2 q1 + 1) a are exact in fp32 (18- and 19-bit products of
+// fp16 values and small integers), and one fused multiply-add gives the sign of their
+// difference. No divide; the sign of x is applied at the end.
+__device__ __forceinline__ v2u quant8_exact(const v8h& x, float a, float lo) {
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = static_cast<float>(x[e]);
+    const float w = fabsf(xf);
+    const float q1 = __builtin_fmaf(w, lo, kRoundMagic) - kRoundMagic;
+    const float d = __builtin_fmaf(2.0f * q1 + 1.0f, a, -254.0f * w);
+    const int qi = static_cast<int>(q1);
+    const int q = qi + ((d < 0.0f || (d == 0.0f && (qi & 1))) ? 1 : 0);
+    c[e] = xf < 0.0f ? -q : q;
+  }
+  v2u o;
+  o[0] = pack4(c[0], c[1], c[2], c[3]);
+  o[1] = pack4(c[4], c[5], c[6], c[7]);
+  return o;
+}
+
+// Lane-wise max of two pairs of u16.
+__device__ __forceinline__ unsigned pk_max_u16(unsigned a, unsigned b) {
+  unsigned d;
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Wave-wide reductions with DPP: row_shr 1, 2, 4, 8 within each row of 16 lanes (lanes
+// shifted in from outside the row read 0, the identity here), then row_bcast15 (lane 15
+// of rows 0 and 2 into rows 1 and 3) and row_bcast31 (lane 31 into rows 2 and 3).
+// After these steps lane i holds the reduction over lanes 0..i.
+template <typename Op>
+__device__ __forceinline__ int wave_scan_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes (lane i: sum of lanes 0..i).
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  return wave_scan_dpp(v, [](int a, int b) { return a + b; });
+}
+// Largest value over the 64 lanes, in every lane (0 is the identity: unsigned values).
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+  const int s = wave_scan_dpp(static_cast<int>(v), [](int a, int b) {
+    return static_cast<int>(max(static_cast<unsigned>(a), static_cast<unsigned>(b)));
+  });
+  return static_cast<unsigned>(__builtin_amdgcn_readlane(s, 63));
+}
+
 // Block barrier for LDS traffic only: waits for this thread's LDS operations, not for
 // its outstanding global loads (__syncthreads would also drain those). The empty asm
 // statements keep the compiler from moving memory accesses across it.
