@@ -197,3 +197,34 @@ def test_timing_hook_counts_main_kernel():
     finally:
         binding.timing_enable(False)
     assert n == 3 and ms > 0
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 4096, 1024), (96, 1040, 528)])
+def test_graph_replay_matches_eager(M, K, N):
+    """A call captured in a HIP graph gives the eager result on every replay, with
+    eager work and synchronizations between the replays (the path issues no memset)."""
+    path = "decode" if binding.is_decode(M, K) else "prefill"
+    announce(f"graph replay {path} M={M} K={K} N={N}")
+    X = dev(planted(51, M, K))
+    Wq, aw = binding.prepare_weight(dev(weight(52, K, N)))
+    ws = binding.make_workspace(M, K, N, 256)
+    want = binding.mixed_matmul(X, Wq, aw, 6.0, 256, workspace=ws).clone()
+    Y = torch.empty_like(want)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.mixed_matmul(X, Wq, aw, 6.0, 256, workspace=ws, out=Y)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.mixed_matmul(X, Wq, aw, 6.0, 256, workspace=ws, out=Y)
+    other = binding.make_workspace(M, K, N, 256)
+    for i in range(4):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+        # eager work between replays, on another workspace
+        binding.mixed_matmul(X, Wq, aw, 6.0, 256, workspace=other)
+        torch.cuda.synchronize()
+    assert binding.read_status(ws)[0] == 0
