@@ -155,6 +155,45 @@ __device__ __forceinline__ v2u quant8_exact(const v8h& x, float a, float lo) {
   return o;
 }
 
+// Clears the halves of v whose bit is set in drop (outlier columns: their codes are 0
+// and they do not enter the row constant). Branch-free: one keep-mask per dword.
+__device__ __forceinline__ void drop_halves(v8h& v, unsigned drop) {
+  v4u u = __builtin_bit_cast(v4u, v);
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    u[d] &= ((drop >> (2 * d)) & 1u ? 0u : 0x0000ffffu) |
+            ((drop >> (2 * d + 1)) & 1u ? 0u : 0xffff0000u);
+  v = __builtin_bit_cast(v8h, u);
+}
+
+// Codes of 8 halves from the bracketing pair (quant8_bracket without its fallback):
+// returns the lower bracket's codes and sets dis != 0 where the pair disagrees.
+__device__ __forceinline__ v2u quant8_fast(const v8h& x, QuantBracket br, unsigned& dis) {
+  unsigned b1[8], b2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = static_cast<float>(x[e]);
+    b1[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.lo, kRoundMagic));
+    b2[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.hi, kRoundMagic));
+  }
+  v2u o;
+  o[0] = pack_low_bytes(b1[0], b1[1], b1[2], b1[3]);
+  o[1] = pack_low_bytes(b1[4], b1[5], b1[6], b1[7]);
+  dis = (o[0] ^ pack_low_bytes(b2[0], b2[1], b2[2], b2[3])) |
+        (o[1] ^ pack_low_bytes(b2[4], b2[5], b2[6], b2[7]));
+  return o;
+}
+
+// The smallest fp16 magnitude (as bits) that is >= t, so that for every finite or
+// infinite half x, |x| >= t exactly when (bits(x) & 0x7fff) >= the result.
+__device__ __forceinline__ unsigned threshold_bits(float t) {
+  if (!(t > 0.0f)) return 0u;
+  if (t > 65504.0f) return 0x7c00u;
+  const _Float16 h = static_cast<_Float16>(t);
+  const unsigned b = __builtin_bit_cast(unsigned short, h);
+  return static_cast<float>(h) < t ? b + 1u : b;
+}
+
 // Lane-wise max of two pairs of u16.
 __device__ __forceinline__ unsigned pk_max_u16(unsigned a, unsigned b) {
   unsigned d;
@@ -186,6 +225,12 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
     return static_cast<int>(max(static_cast<unsigned>(a), static_cast<unsigned>(b)));
   });
   return static_cast<unsigned>(__builtin_amdgcn_readlane(s, 63));
+}
+
+// Largest magnitude (fp16 bits, two per dword) over the wave, as a float.
+__device__ __forceinline__ float wave_max_half_pairs(unsigned pm) {
+  const unsigned h = wave_max_u32(max(pm & 0xffffu, pm >> 16));
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
 }
 
 // Block barrier for LDS traffic only: waits for this thread's LDS operations, not for

@@ -41,16 +41,6 @@ bool decode_supported(int64_t M, int64_t K) {
          rows_per_wave(M) * chunks_per_lane(K) <= 16;  // (2, 8) cannot occur: M > 8 needs K <= 2048
 }
 
-// The smallest fp16 magnitude (as bits) that is >= t, so that for every finite or
-// infinite half x, |x| >= t exactly when (bits(x) & 0x7fff) >= the result.
-__device__ __forceinline__ unsigned threshold_bits(float t) {
-  if (!(t > 0.0f)) return 0u;
-  if (t > 65504.0f) return 0x7c00u;
-  const _Float16 h = static_cast<_Float16>(t);
-  const unsigned b = __builtin_bit_cast(unsigned short, h);
-  return static_cast<float>(h) < t ? b + 1u : b;
-}
-
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
 }

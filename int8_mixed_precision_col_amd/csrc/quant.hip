@@ -23,7 +23,10 @@
 
 namespace i8mm {
 
-// Block (strip, chunk): 64 columns x rows [chunk*rpc, +rpc). 8 threads x 16 B per row.
+// Block (strip, chunk): 64 columns x rows [chunk*rpc, +rpc). 8 threads x 16 B per row;
+// each thread keeps the running magnitude max of its 8 columns as packed u16 (finite
+// and infinite halves order like their magnitude bits) and tests it against the
+// threshold once at the end.
 __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict__ X, int M, int K,
                                                       float t, int rpc,
                                                       uint32_t* __restrict__ partial, int W) {
@@ -32,16 +35,23 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
   const int col0 = blockIdx.x * 64 + cg * 8;
   const int r_begin = blockIdx.y * rpc;
   const int r_end = min(M, r_begin + rpc);
-  unsigned flags = 0;
+  unsigned cm[4] = {0u, 0u, 0u, 0u};
   if (col0 < K) {
 #pragma unroll 8
     for (int r = r_begin + (tid >> 3); r < r_end; r += 32) {
-      v8h v = *reinterpret_cast<const v8h*>(X + static_cast<size_t>(r) * K + col0);
+      const v4u u = *reinterpret_cast<const v4u*>(X + static_cast<size_t>(r) * K + col0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        flags |= static_cast<unsigned>(fabsf(static_cast<float>(v[e])) >= t) << e;
+      for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], u[d] & 0x7fff7fffu);
     }
   }
+  const unsigned tb = threshold_bits(t);
+  unsigned flags = 0;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    flags |= static_cast<unsigned>((cm[d] & 0xffffu) >= tb) << (2 * d);
+    flags |= static_cast<unsigned>((cm[d] >> 16) >= tb) << (2 * d + 1);
+  }
+  if (col0 >= K || r_begin >= r_end) flags = 0;
   flags |= __shfl_xor(flags, 8, 64);
   flags |= __shfl_xor(flags, 16, 64);
   flags |= __shfl_xor(flags, 32, 64);
@@ -64,55 +74,77 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
 // halves per lane, K <= 512 * CH) and read once; CH == 0: streamed twice.
 // Xq goes row-major (ks == 0) or unit-tiled with ks = unit_ks(K) units per row group,
 // in which case the row's K padding is written as zero codes.
+// Outlier columns are cleared in the registers (drop_halves), the row constant is a
+// packed u16 magnitude max reduced over the wave with DPP, and the codes come from the
+// bracketing pair of fused multiply-adds (quant8_fast); groups where the pair
+// disagrees take quant8_exact.
+// Loads a row into registers for quant_one_row<CH> (CH > 0): chunk c = lane + 64 i;
+// unconditional loads at clamped addresses, zeros past the row.
+template <int CH>
+__device__ __forceinline__ void load_row(const _Float16* __restrict__ xr, int K, int lane,
+                                         v8h (&v)[CH > 0 ? CH : 1]) {
+  const int nchunk = K >> 3;
+#pragma unroll
+  for (int i = 0; i < (CH > 0 ? CH : 1); ++i) {
+    const int c = lane + 64 * i;
+    const v8h t = *reinterpret_cast<const v8h*>(xr + min(c, nchunk - 1) * 8);
+    v[i] = c < nchunk ? t : v8h{};
+  }
+}
+
 template <int CH>
 __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, int K,
                                               const uint32_t* words, int8_t* __restrict__ Xq,
-                                              int row, int ks, float* a_x_row, int lane) {
+                                              int row, int ks, float* a_x_row, int lane,
+                                              v8h (&v)[CH > 0 ? CH : 1]) {
   const int nchunk = K >> 3;
   auto dst = [&](int c) -> int8_t* {
     return ks ? Xq + unit_offset(row, c * 8, ks) : Xq + static_cast<size_t>(row) * K + c * 8;
   };
   auto chunk_mask = [&](int c) -> unsigned { return (words[c >> 2] >> ((c & 3) << 3)) & 0xFFu; };
-  auto store_codes = [&](int c, const v8h& v, unsigned mb, float m, float r) {
-    *reinterpret_cast<v2u*>(dst(c)) = quant8(v, mb, m, r);
-  };
-  float m = 0.0f;
+  float m;
   if constexpr (CH > 0) {
-    v8h v[CH];
+    unsigned pm = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
-      v[i] = c < nchunk ? *reinterpret_cast<const v8h*>(xr + c * 8) : v8h{};
+      const unsigned mb = c < nchunk ? chunk_mask(c) : 0u;
+      if (mb) drop_halves(v[i], mb);  // outlier columns are rare
+      const v4u u = __builtin_bit_cast(v4u, v[i]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) pm = pk_max_u16(pm, u[d] & 0x7fff7fffu);
     }
+    m = wave_max_half_pairs(pm);
+    const QuantBracket br = quant_bracket(m);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
-      if (c < nchunk) {
-        const unsigned mb = chunk_mask(c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!((mb >> e) & 1u)) m = fmaxf(m, fabsf(static_cast<float>(v[i][e])));
-      }
-    }
-    m = wave_max(m);
-    const float r = quant_scale(m);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nchunk) store_codes(c, v[i], chunk_mask(c), m, r);
+      unsigned dis;
+      v2u o = quant8_fast(v[i], br, dis);
+      if (dis) o = quant8_exact(v[i], m, br.lo);  // rare; many waves share the code
+      if (c < nchunk) *reinterpret_cast<v2u*>(dst(c)) = o;
     }
   } else {
+    unsigned pm = 0;
     for (int c = lane; c < nchunk; c += 64) {
-      const v8h v = *reinterpret_cast<const v8h*>(xr + c * 8);
+      v8h t = *reinterpret_cast<const v8h*>(xr + c * 8);
       const unsigned mb = chunk_mask(c);
+      if (mb) drop_halves(t, mb);
+      const v4u u = __builtin_bit_cast(v4u, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!((mb >> e) & 1u)) m = fmaxf(m, fabsf(static_cast<float>(v[e])));
+      for (int d = 0; d < 4; ++d) pm = pk_max_u16(pm, u[d] & 0x7fff7fffu);
     }
-    m = wave_max(m);
-    const float r = quant_scale(m);
-    for (int c = lane; c < nchunk; c += 64)
-      store_codes(c, *reinterpret_cast<const v8h*>(xr + c * 8), chunk_mask(c), m, r);
+    m = wave_max_half_pairs(pm);
+    const QuantBracket br = quant_bracket(m);
+    for (int c = lane; c < nchunk; c += 64) {
+      v8h t = *reinterpret_cast<const v8h*>(xr + c * 8);
+      const unsigned mb = chunk_mask(c);
+      if (mb) drop_halves(t, mb);
+      unsigned dis;
+      v2u o = quant8_fast(t, br, dis);
+      if (dis) o = quant8_exact(t, m, br.lo);
+      *reinterpret_cast<v2u*>(dst(c)) = o;
+    }
   }
   if (lane == 0) *a_x_row = m;
   if (ks)
@@ -128,6 +160,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
   int* idx_s = reinterpret_cast<int*>(lds + W);
   __shared__ int wave_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool row_block = static_cast<int>(blockIdx.x) < nrow;
+  const int row = blockIdx.x * 4 + wave;
 
   // 1. column mask = OR of the row-chunk flags
   for (int w = tid; w < W; w += 256) {
@@ -135,15 +169,15 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
     for (int rc = 0; rc < a.R; ++rc) v |= a.partial[static_cast<size_t>(rc) * W + w];
     words[w] = v;
   }
-  __syncthreads();
+  lds_barrier();
   // 2. rank the outlier columns: thread t owns words [t*per, (t+1)*per)
   const int per = (W + 255) / 256;
   const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
   int mine = 0;
   for (int w = w0; w < w1; ++w) mine += __popc(words[w]);
-  const int incl = wave_inclusive_sum(mine);
+  const int incl = wave_prefix_sum(mine);
   if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = incl - mine;
   for (int i = 0; i < wave; ++i) before += wave_tot[i];
   const int count = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
@@ -156,7 +190,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
       ++r;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   if (blockIdx.x == 0) {
     if (tid == 0) {
@@ -169,11 +203,12 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
   // outlier columns actually carried (padded to the 16-wide fp16 MFMA step)
   const int o_pad = min((count + 15) & ~15, a.o_stride);
 
-  if (static_cast<int>(blockIdx.x) < nrow) {
-    const int row = blockIdx.x * 4 + wave;
+  if (row_block) {
     if (row >= a.M) return;
     const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
-    quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane);
+    v8h v[CH > 0 ? CH : 1];
+    if constexpr (CH > 0) load_row<CH>(xr, a.K, lane, v);
+    quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane, v);
     if (a.Xo) {
       _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
       for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
