@@ -142,19 +142,35 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
         print(json.dumps(rec))
 
 
-def prepare(binding, torch, wl, inputs, copies: int):
-    """Draw the workload, move it to the GPU, convert `copies` weights (untimed)."""
+def prepare(binding, torch, wl, inputs, copies: int, time_prepare: bool = False):
+    """Draw the workload, move it to the GPU, convert `copies` weights (untimed by the
+    step clock). With time_prepare, the conversion is also run 3 more times between
+    events and its rate returned (checkpoint-load path)."""
     X, _ = inputs.make_x(wl)
     W = inputs.make_w(wl)
     Xd = torch.from_numpy(X).cuda()
     Wd = torch.from_numpy(W).cuda()
     weights = [binding.prepare_weight(Wd)]
+    prep = None
+    if time_prepare:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            binding.prepare_weight(Wd)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        nbytes = wl.K * wl.N * 2 + wl.K * wl.N + wl.N * 4   # read W once, write Wq and a_w
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        prep = {"ms": ms, "algorithmic_bytes": nbytes, "GB/s": gbs,
+                "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                "note": "two passes over W (column absmax, then quantize + transpose)"}
     for _ in range(copies - 1):
         Wq, aw = weights[0]
         weights.append((Wq.clone(), aw.clone()))
     del Wd
     torch.cuda.synchronize()
-    return X, W, Xd, weights
+    return X, W, Xd, weights, prep
 
 
 def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y):
@@ -216,7 +232,7 @@ def bench_decode(binding, torch, inputs, reps: int) -> dict:
     wl = inputs.WORKLOADS["decode_8x4096"]
     wq_bytes = wl.N * wl.K
     copies = max(1, -(-2 * MALL_BYTES // wq_bytes))          # 32 for 16.8 MB weights
-    _, _, Xd, weights = prepare(binding, torch, wl, inputs, copies)
+    _, _, Xd, weights, _ = prepare(binding, torch, wl, inputs, copies)
     ws = binding.make_workspace(wl.M, wl.K, wl.N, MAX_OUTLIERS)
     Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
     # eager: per-launch kernel time from the library's event hook, for context
@@ -252,12 +268,36 @@ def bench_decode(binding, torch, inputs, reps: int) -> dict:
     per_call_us = e0.elapsed_time(e1) / (reps * copies) * 1e3
     alg_bytes = wl.M * wl.K * 2 + wq_bytes + wl.N * 4 + wl.M * wl.N * 2
     gbs = alg_bytes / (per_call_us * 1e-6) / 1e9
+
+    # the weight-only variant (no activation quantization, no decomposition) on the
+    # same 32 weights, the same way: what the decomposition costs at this shape
+    Yw = torch.empty_like(Y)
+    with torch.cuda.stream(side):
+        for Wq, aw in weights[:2]:
+            binding.weight_only_matmul(Xd, Wq, aw, out=Yw)
+    torch.cuda.current_stream().wait_stream(side)
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for Wq, aw in weights:
+            binding.weight_only_matmul(Xd, Wq, aw, out=Yw)
+    for _ in range(3):
+        gw.replay()
+    e0.record()
+    for _ in range(reps):
+        gw.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wo_us = e0.elapsed_time(e1) / (reps * copies) * 1e3
     return {
         "workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "outlier_cols": count,
         "value": gbs, "unit": "GB/s", "us_per_call": per_call_us,
         "weights_rotated": copies, "graph_replays": reps,
         "algorithmic_bytes_per_call": alg_bytes,
         "eager_us_per_call": eager_us, "eager_kernel_us_hook": hook_us,
+        "weight_only": {"us_per_call": wo_us,
+                        "GB/s": alg_bytes / (wo_us * 1e-6) / 1e9,
+                        "frac_of_hbm_peak": alg_bytes / (wo_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "kernel": "k_weight_only"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
                      "traffic": load_traffic("k_decode", wl.name),
@@ -300,7 +340,7 @@ def main() -> int:
         raise SystemExit(f"{wl.name} is a decode shape; the headline workload is a prefill one")
     log(f"workload {wl.name} M={wl.M} K={wl.K} N={wl.N}: drawing inputs")
     copies = max(1, -(-MALL_BYTES // (wl.N * wl.K)))
-    X, W, Xd, weights = prepare(binding, torch, wl, inputs, copies)
+    X, W, Xd, weights, prep = prepare(binding, torch, wl, inputs, copies, time_prepare=True)
     ws = binding.make_workspace(wl.M, wl.K, wl.N, MAX_OUTLIERS)
     Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
 
@@ -335,6 +375,7 @@ def main() -> int:
                      "traffic": load_traffic("k_gemm", wl.name),
                      "kernel": "k_gemm", "kernel_avg_ms": gemm_avg_ms},
     }
+    result["prepare_weight"] = prep
     del Xd, weights, ws, Y
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -133,6 +133,25 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
 int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
 
 /*
+ * Weight-only int8 product for a handful of tokens: Y = X · Ŵ with
+ * Ŵ[k, n] = Wq[n, k] · w_absmax[n] / 127, no activation quantization and no
+ * outlier decomposition ("What is 8-bit LLM quantization?", What is special about
+ * LLM.int8()?: 8-bit weight storage does not make every activation or operation
+ * int8; Does INT8 always improve speed?: the decoding workload gains from the
+ * smaller weight stream). The comparison point for the decode path above.
+ *   X, M, K       fp16 activations [M, K], 1 <= M <= 16 and M (K + 8) <= 65536
+ *                 (X is staged whole in on-chip memory).
+ *   Wq, w_absmax  unit-tiled int8 weight and fp32 [N] from int8_prepare_weight.
+ *   Y             out, fp16 [M, N] row-major.
+ * Sums: the products of fp16 X and the int8 codes are exact in fp32 and accumulate
+ * in fp32; each output is scaled by w_absmax[n] / 127 once and rounded to fp16.
+ * Errors: as for int8_mixed_matmul (shapes outside the limits above are
+ * INT8MM_E_SHAPE). No workspace.
+ */
+int int8_weight_only_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                            const float* w_absmax, int64_t N, void* Y, hipStream_t stream);
+
+/*
  * Synchronises `stream`, then returns the status word the last
  * int8_mixed_matmul call left in `workspace` (INT8MM_OK or
  * INT8MM_E_TOO_MANY_OUTLIERS), or INT8MM_E_HIP / INT8MM_E_NULL.

@@ -29,6 +29,7 @@ SIGNATURES = {
     "int8_mixed_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _f32, _i64, _p, _p,
                                  ctypes.c_size_t, _p, _p]),
     "int8_mixed_matmul_is_decode": (_int, [_i64, _i64]),
+    "int8_weight_only_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
     "int8mm_read_status": (_int, [_p, _p, _p]),
     "int8mm_strerror": (ctypes.c_char_p, [_int]),
     "int8mm_timing_enable": (_int, [_int]),
@@ -173,6 +174,25 @@ def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold
                                    workspace.data_ptr(), workspace.numel(),
                                    acc_out.data_ptr() if acc_out is not None else None,
                                    _stream(X)), "int8_mixed_matmul")
+    return out
+
+
+def weight_only_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y fp16 [M, N] = X · (Wq · a_w / 127)ᵀ for M <= 16 (weight-only int8, no decomposition)."""
+    _need(X, torch.float16, "X")
+    _need(Wq, torch.int8, "Wq")
+    _need(a_w, torch.float32, "a_w")
+    M, K = X.shape
+    N = a_w.shape[0]
+    if Wq.numel() != int(lib().int8_prepared_weight_bytes(K, N)):
+        raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
+                         f"holds {int(lib().int8_prepared_weight_bytes(K, N))}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(out, torch.float16, "out")
+    _check(lib().int8_weight_only_matmul(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
+                                         out.data_ptr(), _stream(X)), "int8_weight_only_matmul")
     return out
 
 

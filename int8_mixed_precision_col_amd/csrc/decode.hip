@@ -25,6 +25,7 @@ namespace i8mm {
 constexpr int kDecMaxM = 16, kDecMaxK = 8192, kDecMaxMK = 32768;
 constexpr int kDecWaves = 8, kDecThreads = 64 * kDecWaves;
 constexpr int kOutChunk = 64;  // outlier columns staged in LDS per epilogue pass
+constexpr int kPre = kDecThreads / 16;  // outlier columns gathered before the MFMA (32)
 
 static int pow2_at_least(int v) {
   int p = 1;
@@ -115,6 +116,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     wstep[i] = i < nmine ? step : -1;
     wf[i] = *reinterpret_cast<const v4i*>(wunit + static_cast<size_t>(step) * kUnitBytes);
   }
+  // the epilogue's column constant, loaded now so that its latency hides under the rest
+  const float aw_pre = a.a_w[n0 + (tid & 15)];
 
   // 3. outlier flags ("LLM.int8()", Mixed-precision decomposition: a feature column is
   // an outlier when any of its values reaches the threshold). Magnitudes as fp16 bits:
@@ -253,6 +256,16 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       idx_s[r] = static_cast<short>(tid * 32 + b);
     }
   }
+  lds_barrier();
+  // The values of the first kPre outlier columns (one (column, row) pair per thread)
+  // are loaded now, so that their latency overlaps the MFMA (unconditional loads at a
+  // valid column, discarded past the count); they go to LDS with the partials.
+  const int m = (tid >> 4) & 15, nl = tid & 15, n = n0 + nl;
+  const int npre = min(count, kPre);
+  const int pr = tid >> 4, pq = tid & 15;
+  const int pcol = pr < npre ? idx_s[pr] : 0;
+  const int pw = a.Wq[unit_offset(n0 + pq, pcol, ks)];
+  const _Float16 px = a.X[static_cast<size_t>(min(pq, M - 1)) * K + pcol];
 
   // 7. int8 MFMA: D[n_local][m] += Wq[n0 + n_local, k] * Xq[m, k]; the Xq fragments
   // are read (at clamped addresses, discarded past M or K) before the MFMA chain
@@ -272,14 +285,18 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   // 16x16 accumulator layout: lane l, register r -> column m = l % 16, row 4 (l / 16) + r
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][mtok] = acc[r];
+  wo_s[pr * 16 + pq] = pr < npre ? static_cast<float>(pw) : 0.0f;
+  xo_s[pr * 16 + pq] = pr < npre && pq < M ? static_cast<float>(px) : 0.0f;
   lds_barrier();
 
   // 8. epilogue: thread t < 256 -> (token m, output feature n0 + nl). The int32
   // partials of the waves are summed exactly; the outlier columns' product is taken
   // in fp32 from the exact fp16 X and the int8 weight dequantized by a_w / 127.
-  const int m = (tid >> 4) & 15, nl = tid & 15, n = n0 + nl;
   float yo = 0.0f;
-  for (int r0 = 0; r0 < count; r0 += kOutChunk) {  // block-uniform trip count
+  if (tid < 256)
+    for (int r = 0; r < npre; ++r) yo += xo_s[r * 16 + m] * wo_s[r * 16 + nl];
+  for (int r0 = kPre; r0 < count; r0 += kOutChunk) {  // block-uniform trip count
+    lds_barrier();  // the staged values above are read
     const int rn = min(kOutChunk, count - r0);
     for (int t = tid; t < rn * 16; t += kDecThreads) {
       const int r = t >> 4, q = t & 15;
@@ -297,7 +314,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     int s = 0;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) s += red[w][nl][m];
-    const float aw = a.a_w[n];
+    const float aw = aw_pre;
     const float y = static_cast<float>(s) * (rowmax_s[m] * kInvQMax2) * aw + yo * __fdiv_rn(aw, 127.0f);
     a.Y[static_cast<size_t>(m) * a.N + n] =
         overflow ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y);

@@ -197,6 +197,20 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   return timing_end(stream);
 }
 
+int int8_weight_only_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                            const float* w_absmax, int64_t N, void* Y, hipStream_t stream) {
+  if (!X || !Wq || !w_absmax || !Y) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_n(N) || !i8mm::weight_only_supported(M, K)) return INT8MM_E_SHAPE;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y)) return INT8MM_E_ALIGN;
+  i8mm::WeightOnlyArgs a{};
+  a.X = static_cast<const _Float16*>(X); a.M = int(M); a.K = int(K);
+  a.Wq = Wq; a.a_w = w_absmax; a.N = int(N); a.Y = static_cast<_Float16*>(Y);
+  int rc;
+  if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
+  if (i8mm::launch_weight_only(a, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream);
+}
+
 int int8mm_read_status(const void* workspace, int32_t* n_outliers, hipStream_t stream) {
   if (!workspace) return INT8MM_E_NULL;
   if (hipStreamSynchronize(stream) != hipSuccess) return INT8MM_E_HIP;

@@ -67,4 +67,15 @@ struct DecodeArgs {
 bool decode_supported(int64_t M, int64_t K);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+struct WeightOnlyArgs {
+  const _Float16* X;  // [M][K]
+  int M, K;
+  const int8_t* Wq;   // unit-tiled [N][K]
+  const float* a_w;
+  int N;
+  _Float16* Y;        // [M][N]
+};
+bool weight_only_supported(int64_t M, int64_t K);
+hipError_t launch_weight_only(const WeightOnlyArgs& a, hipStream_t s);
+
 }  // namespace i8mm

@@ -16,4 +16,5 @@ from .int8mm_oracle import (  # noqa: F401
     prepare_weight,
     quant_rows,
     quantize,
+    weight_only_matmul,
 )

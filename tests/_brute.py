@@ -68,3 +68,15 @@ def mixed_matmul(X, W, t):
             for n in range(N)] for i in range(M)]
     Y16 = [[to_fp16(y) for y in row] for row in Yex]
     return dict(a_w=a_w, Wq=Wq, O=O, a_x=a_x, Xq=Xq, acc=acc, Yexact=Yex, Y16=Y16)
+
+
+def weight_only_matmul(X, W):
+    """Weight-only int8 product: exact X times the dequantized int8 weight, rounded
+    to fp16 once. Returns the list of rows of exact fp16 values."""
+    K, N = len(W), len(W[0])
+    X = [[Fraction(v) for v in row] for row in X]
+    W = [[Fraction(v) for v in row] for row in W]
+    a_w = [max(abs(W[k][n]) for k in range(K)) for n in range(N)]
+    What = [[Fraction(q_exact(W[k][n], a_w[n])) * a_w[n] / QMAX for n in range(N)]
+            for k in range(K)]
+    return [[to_fp16(sum(row[k] * What[k][n] for k in range(K))) for n in range(N)] for row in X]

@@ -110,3 +110,14 @@ def test_timing_read_without_launches(L):
     ms, n = binding.timing_read()
     assert (ms, n) == (0.0, 0)
     assert L.int8mm_timing_read(None, None) == E_NULL
+
+
+def test_weight_only_rejects(L):
+    wo = L.int8_weight_only_matmul
+    assert wo(None, 4, 32, P, P, 32, P, None) == E_NULL
+    assert wo(P, 17, 32, P, P, 32, P, None) == E_SHAPE      # decode shapes only
+    assert wo(P, 0, 32, P, P, 32, P, None) == E_SHAPE
+    assert wo(P, 4, 24, P, P, 32, P, None) == E_SHAPE       # K not a multiple of 16
+    assert wo(P, 4, 32, P, P, 24, P, None) == E_SHAPE       # N not a multiple of 16
+    assert wo(UNALIGNED, 4, 32, P, P, 32, P, None) == E_ALIGN
+    assert wo(P, 4, 32, P, P, 32, UNALIGNED, None) == E_ALIGN

@@ -228,3 +228,17 @@ def test_graph_replay_matches_eager(M, K, N):
         binding.mixed_matmul(X, Wq, aw, 6.0, 256, workspace=other)
         torch.cuda.synchronize()
     assert binding.read_status(ws)[0] == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 4096, 4096), (1, 32, 16), (16, 1040, 528),
+                                   (5, 12288, 64), (3, 16, 48)])
+def test_weight_only_parity(M, K, N):
+    """Weight-only int8 (no activation quantization) against the oracle's fp16(X @ W^)."""
+    announce(f"weight-only M={M} K={K} N={N}")
+    X = planted(M + K, M, K, n_dims=3)
+    W = weight(M + N, K, N)
+    Wq_ref, aw_ref = oracle.prepare_weight(W)
+    want = oracle.weight_only_matmul(X, Wq_ref, aw_ref)
+    Wq, aw = binding.prepare_weight(dev(W))
+    Y = binding.weight_only_matmul(dev(X), Wq, aw)
+    check_y(host(Y), want)

@@ -327,3 +327,29 @@ def test_weight_memory_halves():
     W = f16(np.ones((64, 48)))
     Wq, a_w = oracle.prepare_weight(W)
     assert Wq.nbytes * 2 == W.nbytes and a_w.nbytes == 4 * 48
+
+
+# ---------------------------------------------------------------- weight-only variant
+
+@pytest.mark.parametrize("seed,M,K,N", [(11, 1, 16, 16), (12, 3, 32, 16), (13, 4, 16, 32)])
+def test_weight_only_matches_exact_brute_force(seed, M, K, N):
+    """fp16(X @ dequantized W) against the exact rational product rounded once."""
+    X, W, _ = _brute_case(seed, M, K, N, 6.0, adversarial=True)
+    Wq, a_w = oracle.prepare_weight(W)
+    got = oracle.weight_only_matmul(X, Wq, a_w)
+    b = _brute.weight_only_matmul(X.astype(np.float64).tolist(), W.astype(np.float64).tolist())
+    Yb = np.array([[float(v) for v in row] for row in b], dtype=np.float16)
+    ulps = np.abs(got.view(np.int16).astype(np.int32) - Yb.view(np.int16).astype(np.int32))
+    assert ulps.max() <= 1 and (ulps == 0).mean() > 0.9
+
+
+def test_weight_only_is_the_all_outlier_decomposition_and_differs_from_it_otherwise():
+    """Every column an outlier (t = 0) leaves only the 16-bit product over dequantized
+    weights, which is the weight-only product; with real outliers they differ."""
+    rng = np.random.default_rng(21)
+    X = f16(rng.standard_normal((6, 64)))
+    X[:, 5] = 40.0
+    Wq, a_w = oracle.prepare_weight(f16(rng.standard_normal((64, 48)) * 0.05))
+    wo = oracle.weight_only_matmul(X, Wq, a_w)
+    assert np.array_equal(wo, oracle.mixed_matmul(X, Wq, a_w, 0.0)["Y"])
+    assert not np.array_equal(wo, oracle.mixed_matmul(X, Wq, a_w, 6.0)["Y"])
