@@ -133,6 +133,34 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
 int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
 
 /*
+ * The activation side once, for several weights that share the same input (the
+ * projections fed by one X: [Abstract], the decomposition applies to the
+ * feed-forward and attention projection layers). int8_quantize_activations runs
+ * the outlier detection and row quantization of int8_mixed_matmul into `state`;
+ * int8_mixed_matmul_q then runs the weight side (outlier weight gather, int8 MFMA
+ * GEMM, fp16 outlier product, dequant epilogue) for one weight from that state.
+ * Y equals int8_mixed_matmul's bit for bit when int8_mixed_matmul takes its
+ * multi-kernel path (M > 16 or large K); for decode shapes the same values are
+ * reached through the GEMM instead of the single decode kernel.
+ *   state         device buffer of int8_quant_state_bytes(M, K, max_outliers),
+ *                 written by int8_quantize_activations, read by int8_mixed_matmul_q;
+ *                 it holds the status word (int8mm_read_status works on it).
+ *   workspace     (int8_mixed_matmul_q) at least int8_mixed_matmul_q_workspace_bytes(N,
+ *                 max_outliers) bytes: the weight's dequantized outlier rows.
+ * M, K, max_outliers and the threshold's outcome are those of the quantization
+ * call; arguments are validated as for int8_mixed_matmul.
+ */
+size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers);
+int int8_quantize_activations(const void* X, int64_t M, int64_t K, float threshold,
+                              int64_t max_outliers, void* state, size_t state_bytes,
+                              hipStream_t stream);
+size_t int8_mixed_matmul_q_workspace_bytes(int64_t N, int64_t max_outliers);
+int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_outliers,
+                        const int8_t* Wq, const float* w_absmax, int64_t N, void* Y,
+                        void* workspace, size_t workspace_bytes, int32_t* acc_i32,
+                        hipStream_t stream);
+
+/*
  * Weight-only int8 product for a handful of tokens: Y = X · Ŵ with
  * Ŵ[k, n] = Wq[n, k] · w_absmax[n] / 127, no activation quantization and no
  * outlier decomposition ("What is 8-bit LLM quantization?", What is special about

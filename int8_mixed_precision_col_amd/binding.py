@@ -30,6 +30,11 @@ SIGNATURES = {
                                  ctypes.c_size_t, _p, _p]),
     "int8_mixed_matmul_is_decode": (_int, [_i64, _i64]),
     "int8_weight_only_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
+    "int8_quant_state_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "int8_quantize_activations": (_int, [_p, _i64, _i64, _f32, _i64, _p, ctypes.c_size_t, _p]),
+    "int8_mixed_matmul_q_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "int8_mixed_matmul_q": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, ctypes.c_size_t,
+                                   _p, _p]),
     "int8mm_read_status": (_int, [_p, _p, _p]),
     "int8mm_strerror": (ctypes.c_char_p, [_int]),
     "int8mm_timing_enable": (_int, [_int]),
@@ -194,6 +199,48 @@ def weight_only_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor,
     _check(lib().int8_weight_only_matmul(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
                                          out.data_ptr(), _stream(X)), "int8_weight_only_matmul")
     return out
+
+
+class QuantizedActivations:
+    """X quantized once (outlier columns, row constants, Xq, outlier values) for
+    several int8_mixed_matmul_q calls; holds the device state buffer."""
+
+    def __init__(self, X: torch.Tensor, threshold: float = 6.0, max_outliers: int = 256):
+        _need(X, torch.float16, "X")
+        self.M, self.K = X.shape
+        self.max_outliers = max_outliers
+        nbytes = int(lib().int8_quant_state_bytes(self.M, self.K, max_outliers))
+        if nbytes == 0:
+            raise ValueError(f"bad shape: M={self.M} K={self.K} max_outliers={max_outliers}")
+        self.state = torch.empty((nbytes,), dtype=torch.uint8, device=X.device)
+        _check(lib().int8_quantize_activations(X.data_ptr(), self.M, self.K, float(threshold),
+                                               max_outliers, self.state.data_ptr(), nbytes,
+                                               _stream(X)), "int8_quantize_activations")
+
+    def matmul(self, Wq: torch.Tensor, a_w: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None,
+               acc_out: torch.Tensor | None = None) -> torch.Tensor:
+        """Y fp16 [M, N] for one prepared weight, from this quantized X."""
+        _need(Wq, torch.int8, "Wq")
+        _need(a_w, torch.float32, "a_w")
+        N = a_w.shape[0]
+        if Wq.numel() != int(lib().int8_prepared_weight_bytes(self.K, N)):
+            raise ValueError("Wq does not match (K, N)")
+        wb = int(lib().int8_mixed_matmul_q_workspace_bytes(N, self.max_outliers))
+        if workspace is None:
+            workspace = torch.empty((wb,), dtype=torch.uint8, device=Wq.device)
+        _need(workspace, torch.uint8, "workspace")
+        if out is None:
+            out = torch.empty((self.M, N), dtype=torch.float16, device=Wq.device)
+        _need(out, torch.float16, "out")
+        if acc_out is not None:
+            _need(acc_out, torch.int32, "acc_out")
+        _check(lib().int8_mixed_matmul_q(self.state.data_ptr(), self.M, self.K, self.max_outliers,
+                                         Wq.data_ptr(), a_w.data_ptr(), N, out.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(),
+                                         acc_out.data_ptr() if acc_out is not None else None,
+                                         _stream(Wq)), "int8_mixed_matmul_q")
+        return out
 
 
 def read_status(workspace: torch.Tensor) -> tuple[int, int]:

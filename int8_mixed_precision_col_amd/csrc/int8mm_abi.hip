@@ -43,13 +43,10 @@ struct Layout {
 
 // Workspace: [status, count] header, then (prefill only) the row-chunk column flags,
 // a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and WoT, each 256-byte aligned.
-Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+// A quantized-activation state (int8_quantize_activations) is the same without WoT.
+Layout prefill_layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   Layout L;
   size_t off = 256;
-  if (i8mm::decode_supported(M, K)) {
-    L.total = off;
-    return L;
-  }
   const size_t W = (K + 31) / 32;
   const size_t m_rows = (M + 15) & ~int64_t(15);
   L.R = mask_row_chunks(M, K);
@@ -61,6 +58,15 @@ Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   L.wot = off;     off += round256(size_t(N) * L.o_stride * 2);
   L.total = off;
   return L;
+}
+
+Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+  if (i8mm::decode_supported(M, K)) {
+    Layout L;
+    L.total = 256;
+    return L;
+  }
+  return prefill_layout(M, K, N, max_outliers);
 }
 
 // Optional event timing of the main kernel.
@@ -192,6 +198,82 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   g.Xo = xo; g.WoT = wot; g.o_stride = L.o_stride;
   g.count = status + 1; g.max_outliers = int(max_outliers);
   g.Y = y; g.acc_out = acc_i32;
+  if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
+  if (i8mm::launch_gemm(g, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream);
+}
+
+size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers) {
+  if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return 0;
+  return prefill_layout(M, K, 0, max_outliers).wot;  // everything before WoT
+}
+
+size_t int8_mixed_matmul_q_workspace_bytes(int64_t N, int64_t max_outliers) {
+  if (bad_n(N) || max_outliers < 0 || max_outliers > kMaxOutliers) return 0;
+  const size_t o_stride = (max_outliers + 15) & ~int64_t(15);
+  return round256(size_t(N) * o_stride * 2 + 16);
+}
+
+int int8_quantize_activations(const void* X, int64_t M, int64_t K, float threshold,
+                              int64_t max_outliers, void* state, size_t state_bytes,
+                              hipStream_t stream) {
+  if (!X || !state) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
+  if (!aligned16(X) || !aligned16(state)) return INT8MM_E_ALIGN;
+  const Layout L = prefill_layout(M, K, 0, max_outliers);
+  if (state_bytes < L.wot) return INT8MM_E_WORKSPACE;
+  char* ws = static_cast<char*>(state);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+  const _Float16* x = static_cast<const _Float16*>(X);
+  uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
+  if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
+    return INT8MM_E_HIP;
+  i8mm::QuantRowsArgs q{};
+  q.X = x; q.M = int(M); q.K = int(K);
+  q.partial = partial; q.R = L.R;
+  q.Xq = reinterpret_cast<int8_t*>(ws + L.xq); q.xq_tiled = 1;
+  q.a_x = reinterpret_cast<float*>(ws + L.a_x);
+  q.idx_out = nullptr; q.count_out = status + 1; q.status_out = status;
+  q.max_outliers = int(max_outliers);
+  q.Xo = reinterpret_cast<_Float16*>(ws + L.xo); q.o_stride = L.o_stride;
+  q.WoT = nullptr;
+  return hip_status(i8mm::launch_quant_rows(q, stream));
+}
+
+int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_outliers,
+                        const int8_t* Wq, const float* w_absmax, int64_t N, void* Y,
+                        void* workspace, size_t workspace_bytes, int32_t* acc_i32,
+                        hipStream_t stream) {
+  if (!state || !Wq || !w_absmax || !Y || !workspace) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  if (!aligned16(state) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
+      !aligned16(workspace) || (acc_i32 && !aligned16(acc_i32)))
+    return INT8MM_E_ALIGN;
+  if (workspace_bytes < int8_mixed_matmul_q_workspace_bytes(N, max_outliers))
+    return INT8MM_E_WORKSPACE;
+  const Layout L = prefill_layout(M, K, N, max_outliers);
+  const char* st = static_cast<const char*>(state);
+  const int32_t* status = reinterpret_cast<const int32_t*>(st + L.status);
+  _Float16* wot = static_cast<_Float16*>(workspace);
+  // the weight-specific part of the outlier product: dequantized outlier rows of Wq
+  i8mm::QuantRowsArgs q{};
+  q.M = int(M); q.K = int(K);
+  q.partial = reinterpret_cast<const uint32_t*>(st + L.partial); q.R = L.R;
+  q.gather_only = 1;
+  q.count_out = nullptr; q.status_out = nullptr; q.idx_out = nullptr;
+  q.max_outliers = int(max_outliers);
+  q.o_stride = L.o_stride;
+  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
+  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
+  i8mm::GemmArgs g{};
+  g.Wq = Wq; g.Xq = reinterpret_cast<const int8_t*>(st + L.xq); g.M = int(M); g.N = int(N);
+  g.K = int(K);
+  g.a_x = reinterpret_cast<const float*>(st + L.a_x); g.a_w = w_absmax;
+  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo); g.WoT = wot; g.o_stride = L.o_stride;
+  g.count = status + 1; g.max_outliers = int(max_outliers);
+  g.Y = static_cast<_Float16*>(Y); g.acc_out = acc_i32;
+  int rc;
   if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
   if (i8mm::launch_gemm(g, stream) != hipSuccess) return INT8MM_E_HIP;
   return timing_end(stream);

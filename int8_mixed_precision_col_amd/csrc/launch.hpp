@@ -33,6 +33,7 @@ struct QuantRowsArgs {
   const float* a_w;
   int N;
   _Float16* WoT;        // [N][o_stride] fp16 dequantized outlier weight rows
+  int gather_only;      // 1: no row blocks (X, Xq, a_x, Xo unused; count_out may be null)
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
 

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
 
   if (blockIdx.x == 0) {
     if (tid == 0) {
-      a.count_out[0] = count;
+      if (a.count_out) a.count_out[0] = count;
       if (a.status_out) a.status_out[0] = count > a.max_outliers ? 7 : 0;
     }
     if (a.idx_out)
@@ -248,12 +248,13 @@ hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s) {
   const int W = (a.K + 31) / 32;
   const int o_lds = a.o_stride > a.max_outliers ? a.o_stride : a.max_outliers;
   const size_t lds = static_cast<size_t>(W + o_lds) * 4;
-  const int nrow = (a.M + 3) / 4;
+  const int nrow = a.gather_only ? 0 : (a.M + 3) / 4;
   const int ngather = a.WoT ? (a.N + 255) / 256 : 0;
   const dim3 grid(nrow + ngather), block(256);
   const int per_lane = (a.K / 8 + 63) / 64;
 #define I8MM_QR(CHV) hipLaunchKernelGGL(k_quant_rows<CHV>, grid, block, lds, s, a, W, o_lds, nrow)
-  if (per_lane <= 1) I8MM_QR(1);
+  if (a.gather_only) I8MM_QR(0);  // no row blocks
+  else if (per_lane <= 1) I8MM_QR(1);
   else if (per_lane <= 2) I8MM_QR(2);
   else if (per_lane <= 4) I8MM_QR(4);
   else if (per_lane <= 8) I8MM_QR(8);

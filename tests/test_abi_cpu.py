@@ -121,3 +121,23 @@ def test_weight_only_rejects(L):
     assert wo(P, 4, 32, P, P, 24, P, None) == E_SHAPE       # N not a multiple of 16
     assert wo(UNALIGNED, 4, 32, P, P, 32, P, None) == E_ALIGN
     assert wo(P, 4, 32, P, P, 32, UNALIGNED, None) == E_ALIGN
+
+
+def test_quantize_once_rejects_and_sizes(L):
+    assert L.int8_quant_state_bytes(0, 64, 16) == 0
+    assert L.int8_quant_state_bytes(4096, 12288, 256) > 4096 * 12288   # holds Xq
+    assert L.int8_mixed_matmul_q_workspace_bytes(512, 256) >= 512 * 256 * 2
+    assert L.int8_mixed_matmul_q_workspace_bytes(24, 16) == 0
+    qa = L.int8_quantize_activations
+    nb = L.int8_quant_state_bytes(64, 256, 16)
+    assert qa(None, 64, 256, 6.0, 16, P, nb, None) == E_NULL
+    assert qa(P, 64, 250, 6.0, 16, P, nb, None) == E_SHAPE
+    assert qa(P, 64, 256, -1.0, 16, P, nb, None) == E_THR
+    assert qa(P, 64, 256, 6.0, 16, UNALIGNED, nb, None) == E_ALIGN
+    assert qa(P, 64, 256, 6.0, 16, P, nb - 1, None) == E_WS
+    mq = L.int8_mixed_matmul_q
+    wb = L.int8_mixed_matmul_q_workspace_bytes(128, 16)
+    assert mq(P, 64, 256, 16, None, P, 128, P, P, wb, None, None) == E_NULL
+    assert mq(P, 64, 256, 16, P, P, 120, P, P, wb, None, None) == E_SHAPE
+    assert mq(P, 64, 256, 16, P, P, 128, UNALIGNED, P, wb, None, None) == E_ALIGN
+    assert mq(P, 64, 256, 16, P, P, 128, P, P, wb - 1, None, None) == E_WS

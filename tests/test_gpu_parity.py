@@ -242,3 +242,29 @@ def test_weight_only_parity(M, K, N):
     Wq, aw = binding.prepare_weight(dev(W))
     Y = binding.weight_only_matmul(dev(X), Wq, aw)
     check_y(host(Y), want)
+
+
+@pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
+                                    (64, 8192, (256,))])
+def test_quantize_once_feeds_several_weights(M, K, Ns):
+    """One activation quantization, several weights: each product equals the oracle
+    (acc bit-exact, Y within tolerance) and, on the multi-kernel path, the one-call
+    int8_mixed_matmul bit for bit."""
+    announce(f"quantize once M={M} K={K} N={Ns}")
+    X = planted(M + K, M, K, n_dims=4)
+    Xd = dev(X)
+    qa = binding.QuantizedActivations(Xd, 6.0, 256)
+    q_ref = oracle.quant_rows(X, 6.0)
+    assert binding.read_status(qa.state) == (0, q_ref["count"])
+    for i, N in enumerate(Ns):
+        W = weight(M + N + i, K, N)
+        Wq_ref, aw_ref = oracle.prepare_weight(W)
+        ref = oracle.mixed_matmul(X, Wq_ref, aw_ref, 6.0)
+        Wq, aw = binding.prepare_weight(dev(W))
+        acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        Y = qa.matmul(Wq, aw, acc_out=acc)
+        assert np.array_equal(host(acc), ref["acc"])
+        check_y(host(Y), ref["Y"])
+        if not binding.is_decode(M, K):
+            Y1 = binding.mixed_matmul(Xd, Wq, aw, 6.0, 256)
+            assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
