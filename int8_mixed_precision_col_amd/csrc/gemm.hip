@@ -3,8 +3,9 @@
 
 namespace i8mm {
 
-// Large problems: 256 x 256 tiles, 8 waves (two per SIMD, 128 x 64 each), 3-stage ring.
-using CfgL = GemmCfg<256, 256, 64, 2, 4, 3>;
+// Large problems: 256 x 256 tiles, 8 waves (two per SIMD, 128 x 64 each), 4-stage ring
+// (128 KB of LDS).
+using CfgL = GemmCfg<256, 256, 64, 2, 4, 4>;
 // Small or skinny problems: 128 x 128 tiles, 4 waves.
 using CfgS = GemmCfg<128, 128, 64, 2, 2, 3>;
 

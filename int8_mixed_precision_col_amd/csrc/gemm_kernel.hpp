@@ -216,6 +216,24 @@ struct GemmBlock {
                      I8MM_LDS(base + C::A_BYTES + (i * C::NW + wave) * 1024));
   }
 
+  // One DMA instruction (q < AI: A chunk q, else B chunk q - AI) of slab kt into stage S.
+  template <int S>
+  __device__ __forceinline__ void issue_one(int kt, int q) {
+    const int k0 = kt * C::BK;
+    const size_t step = static_cast<size_t>(kt) * (C::BK / kUnitK) * kUnitBytes;
+    const int kpad = unit_ks(g.K) * kUnitK;
+    char* base = stage_buf<C, S>();
+    const int8_t* zero = reinterpret_cast<const int8_t*>(kZero16);
+    if (q < C::AI) {
+      dma16<C::CPOL>(k0 + a_k[q] < kpad ? a_src[q] + step : zero,
+                     I8MM_LDS(base + (q * C::NW + wave) * 1024));
+    } else {
+      const int i = q - C::AI;
+      dma16<C::CPOL>(k0 + b_k[i] < kpad ? b_src[i] + step : zero,
+                     I8MM_LDS(base + C::A_BYTES + (i * C::NW + wave) * 1024));
+    }
+  }
+
   struct Frags {
     v4i a[C::BN], b[C::BM];
   };
@@ -234,6 +252,28 @@ struct GemmBlock {
       f.b[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 32, c));
   }
 
+  // The MFMAs of one substep with the DMA of slab kt into stage S spread between them:
+  // issued as a burst right after the barrier, the DMA instructions of all waves stall
+  // their issue queues together and the matrix cores idle meanwhile.
+  template <int S>
+  __device__ __forceinline__ void mma_dma(const Frags& f, int kt) {
+    constexpr int NQ = C::AI + C::BI, NMM = C::BN * C::BM;
+    constexpr int EVERY = NMM / NQ > 0 ? NMM / NQ : 1;
+#pragma unroll
+    for (int i = 0; i < C::BN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::BM; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        if ((i * C::BM + j) % EVERY == EVERY - 1 && (i * C::BM + j) / EVERY < NQ) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one<S>(kt, (i * C::BM + j) / EVERY);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+    for (int q = NMM / EVERY; q < NQ; ++q) issue_one<S>(kt, q);
+  }
+
   __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
     for (int i = 0; i < C::BN; ++i)
@@ -246,9 +286,9 @@ struct GemmBlock {
   // Substep s + 1's fragments are read while substep s multiplies. Before the last
   // substep (whose fragments are in registers by then): wait until slab kt + 1 has
   // landed (this thread's DMA, then the barrier for everyone else's; the slabs up to
-  // kt + STAGES - 1 may still be in flight), refill stage CUR - free now that every
-  // wave has read all of slab kt - with slab kt + STAGES, and read slab kt + 1's first
-  // fragments while the last MFMAs of slab kt run.
+  // kt + STAGES - 1 may still be in flight), read slab kt + 1's first fragments, and
+  // run the last MFMAs of slab kt with the refill of stage CUR - free now that every
+  // wave has read all of slab kt - by slab kt + STAGES spread between them.
   template <int CUR>
   __device__ __forceinline__ void step(int kt, Frags& f) {
     constexpr int S = C::STAGES, NS = C::BK / 32;
@@ -269,10 +309,9 @@ struct GemmBlock {
       f = nxt;
     }
     wait_and_barrier<(S - 2) * (C::AI + C::BI)>();
-    issue<CUR>(kt + S);
     load_frags<(CUR + 1) % S>(nxt, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f);
+    mma_dma<CUR>(f, kt + S);
     __builtin_amdgcn_sched_barrier(0);
     f = nxt;
   }
