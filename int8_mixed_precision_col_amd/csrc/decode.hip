@@ -39,7 +39,7 @@ static int chunks_per_lane(int64_t K) { return pow2_at_least(static_cast<int>((K
 
 bool decode_supported(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K <= kDecMaxK && M * K <= kDecMaxMK &&
-         rows_per_wave(M) * chunks_per_lane(K) <= 16;  // (2, 8) cannot occur: M > 8 needs K <= 2048
+         rows_per_wave(M) * chunks_per_lane(K) <= 16;
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
@@ -269,19 +269,24 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 
   // 7. int8 MFMA: D[n_local][m] += Wq[n0 + n_local, k] * Xq[m, k]; the Xq fragments
   // are read (at clamped addresses, discarded past M or K) before the MFMA chain
+  // (in batches of at most 8 steps, to bound the registers the fragments take)
   const int mtok = lane & 15;
-  v4i xf[SPW];
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int k = 64 * max(wstep[i], 0) + kl;
-    const v4i t = *reinterpret_cast<const v4i*>(xq_s + min(mtok, M - 1) * xs + min(k, K - 16));
-    xf[i] = (mtok < M && k < K) ? t : v4i{};
-  }
+  constexpr int XB = SPW < 8 ? SPW : 8;
   v4i acc = v4i{};
 #pragma unroll
-  for (int i = 0; i < SPW; ++i)
-    if (wstep[i] >= 0)  // wave-uniform
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], xf[i], acc, 0, 0, 0);
+  for (int i0 = 0; i0 < SPW; i0 += XB) {
+    v4i xf[XB];
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int k = 64 * max(wstep[i0 + i], 0) + kl;
+      const v4i t = *reinterpret_cast<const v4i*>(xq_s + min(mtok, M - 1) * xs + min(k, K - 16));
+      xf[i] = (mtok < M && k < K) ? t : v4i{};
+    }
+#pragma unroll
+    for (int i = 0; i < XB; ++i)
+      if (wstep[i0 + i] >= 0)  // wave-uniform
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i0 + i], xf[i], acc, 0, 0, 0);
+  }
   // 16x16 accumulator layout: lane l, register r -> column m = l % 16, row 4 (l / 16) + r
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][mtok] = acc[r];
@@ -340,7 +345,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();                                                       \
   }
   I8MM_DEC(1, 1) I8MM_DEC(1, 2) I8MM_DEC(1, 4) I8MM_DEC(1, 8) I8MM_DEC(1, 16)
-  I8MM_DEC(2, 1) I8MM_DEC(2, 2) I8MM_DEC(2, 4)
+  I8MM_DEC(2, 1) I8MM_DEC(2, 2) I8MM_DEC(2, 4) I8MM_DEC(2, 8)
 #undef I8MM_DEC
   return hipErrorInvalidValue;
 }

@@ -102,6 +102,7 @@ def _mixed(X, W, t, mo=256, workspace=None):
 CASES = [
     # (M, K, N): decode kernel
     (16, 1024, 1024), (5, 1040, 528), (8, 4096, 4096), (1, 32, 16), (16, 2048, 80),
+    (4, 8192, 256), (3, 8176, 48), (9, 3600, 144),
     # prefill, small tiles
     (300, 1040, 528), (17, 256, 4112), (64, 8192, 256), (1, 12288, 64),
     # prefill, large tiles
