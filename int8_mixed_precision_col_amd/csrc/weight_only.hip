@@ -21,7 +21,7 @@
 
 namespace i8mm {
 
-constexpr int kWoWaves = 4, kWoBatch = 16;
+constexpr int kWoWaves = 16, kWoBatch = 4;
 
 // 4 int8 codes (one dword) -> 4 fp16 of the same values, as 2 dwords.
 __device__ __forceinline__ v2u int8x4_to_half(unsigned d) {
