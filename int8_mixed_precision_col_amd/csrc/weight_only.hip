@@ -9,13 +9,13 @@
 // Wq[n, k] a_w[n] / 127, with fp32 accumulation; the constant is applied once per
 // output.
 //
-// One block per 16 output features (one 16-row group of the unit-tiled Wq), 4 waves.
+// One block per 16 output features (one 16-row group of the unit-tiled Wq), 16 waves.
 // X is staged in LDS first (its loads go out before the weight stream). Wave w takes
-// k-steps w, w + 4, ... (64 columns each) in batches of kBatch: every
+// k-steps w, w + 16, ... (64 columns each) in batches of kWoBatch: every
 // weight load reads one whole 1 KB unit, the int8 bytes become exact fp16 values
 // (1024 + (q + 128) built bitwise, then 1152 subtracted in packed fp16), and each
 // step is two v_mfma_f32_16x16x32_f16 with the unit as the 16-row operand and 16
-// tokens of X (zero past M) as the other. Partials of the 4 waves are summed in LDS.
+// tokens of X (zero past M) as the other. Partials of the waves are summed in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
