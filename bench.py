@@ -47,6 +47,11 @@ def source_digest(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
+def array_digest(a: np.ndarray) -> str:
+    """First 16 hex digits of the SHA-256 of an array's bytes (C order)."""
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+
+
 KERNEL_SOURCES = {
     "k_gemm": ("gemm.hip", "gemm_kernel.hpp", "common.hpp"),
     "k_decode": ("decode.hip", "common.hpp"),
@@ -376,6 +381,8 @@ def main() -> int:
                      "kernel": "k_gemm", "kernel_avg_ms": gemm_avg_ms},
     }
     result["prepare_weight"] = prep
+    # the GPU path and the CPU baseline below read these same host arrays
+    result["inputs_sha256_16"] = {"X_fp16": array_digest(X), "W_fp16": array_digest(W)}
     del Xd, weights, ws, Y
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -17,6 +17,8 @@
 //      the outer-product dequant and adds the outlier columns' product in fp32
 //      (exact fp16 X times the int8 weight dequantized by a_w / 127, both staged in
 //      LDS) before the single rounding to fp16.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,40 +34,82 @@ static int pow2_at_least(int v) {
   while (p < v) p <<= 1;
   return p;
 }
-static int rows_per_wave(int64_t M) {
-  return pow2_at_least(static_cast<int>((M + kDecWaves - 1) / kDecWaves));
+// token rows held per thread: M rounded up to a power of two, at least 2
+static int rows_held(int64_t M) { return max(2, pow2_at_least(static_cast<int>(M))); }
+// MFMA k-steps (64 columns each) per wave: ceil(K / 512) rounded up, at least 2
+static int steps_per_wave(int64_t K) {
+  return max(2, pow2_at_least(static_cast<int>((K + 511) / 512)));
 }
-static int chunks_per_lane(int64_t K) { return pow2_at_least(static_cast<int>((K + 511) / 512)); }
 
+// M K <= 32768 keeps Xq and the registers of X within budget (K > 4096 allows M <= 7).
 bool decode_supported(int64_t M, int64_t K) {
-  return M >= 1 && M <= kDecMaxM && K <= kDecMaxK && M * K <= kDecMaxMK &&
-         rows_per_wave(M) * chunks_per_lane(K) <= 16;
+  return M >= 1 && M <= kDecMaxM && K <= kDecMaxK && M * K <= kDecMaxMK;
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
 }
 
-// RW: rows per wave (wave w owns rows w + 8 i), CL: 8-column chunks per lane (lane l
-// owns chunks l + 64 j). Wave w's MFMA k-steps are w, w + 8, ... (at most CL of them).
-template <int RW, int CL>
+typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+typedef short v2ss __attribute__((ext_vector_type(2)));
+
+// Per half of a dword of magnitudes (fp16 bits, sign cleared): 0xffff where the
+// magnitude is below the threshold bits (tb2 holds them in both halves), 0 where it
+// reaches them. Both are below 2^15, so mag - tb wraps (sets bit 15) exactly when
+// mag < tb; an arithmetic shift spreads that bit over its half.
+__device__ __forceinline__ unsigned keep_halves(unsigned mag2, unsigned tb2) {
+  const v2us d = __builtin_bit_cast(v2us, mag2) - __builtin_bit_cast(v2us, tb2);
+  return __builtin_bit_cast(unsigned, __builtin_bit_cast(v2ss, d) >> (v2ss){15, 15});
+}
+
+// Largest value over the 64 lanes of each of N unsigned values, in every lane: the
+// DPP steps of wave_scan_dpp, taken for all N values before the next step so that
+// the independent chains fill each other's DPP wait states.
+template <int N>
+__device__ __forceinline__ void wave_max_u32_n(unsigned (&v)[N]) {
+  auto step = [&](auto ctrl, auto rmask, auto bound) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      v[i] = max(v[i], static_cast<unsigned>(__builtin_amdgcn_update_dpp(
+                           0, static_cast<int>(v[i]), decltype(ctrl)::value,
+                           decltype(rmask)::value, 0xF, decltype(bound)::value)));
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  step(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xF>{}, T{});
+  step(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xF>{}, T{});
+  step(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xF>{}, T{});
+  step(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xF>{}, T{});
+  step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{}, F{});
+  step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{}, F{});
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(v[i]), 63));
+}
+
+// MR: token rows held per thread (M <= MR), SPW: MFMA k-steps per wave (slots for the
+// weight units). Thread t owns the 8-column chunks c = 64 ((w + xrot) mod 8) + l + 512 j
+// (w its wave, l its lane, j < CC) of every row, so a chunk's outlier test over all
+// rows and its keep-mask are computed once, in registers.
+template <int MR, int SPW>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
-  constexpr int SPW = CL;
+  constexpr int CC = SPW > 8 ? 2 : 1;  // chunks per thread: K <= 4096 needs one
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int red[kDecWaves][16][17];
   __shared__ int wave_tot[kDecWaves];
+  __shared__ unsigned rmax_w[kDecWaves][MR];  // each wave's row maxima (fp16 bits)
   __shared__ float rowmax_s[kDecMaxM];
   const int K = a.K, M = a.M;
   const int W = (K + 31) / 32, nchunk = K / 8, xs = K + 16;
-  // LDS: Xq [M][K + 16] | per-chunk flag bytes of each wave [nchunk][8] | combined mask
-  // words [W] | outlier column list [K] (short) | outlier staging
+  const int nflag = (nchunk + 3) & ~3;
+  // LDS: Xq [M][K + 16] | outlier bits, one byte per chunk [nflag] | mask words [W] |
+  // outlier column list [K] (short) | outlier staging | sink
   int8_t* xq_s = reinterpret_cast<int8_t*>(lds);
   const int off_flag = (M * xs + 15) & ~15;
   unsigned char* flag_s = reinterpret_cast<unsigned char*>(lds + off_flag);
-  uint32_t* mask_s = reinterpret_cast<uint32_t*>(lds + off_flag + nchunk * kDecWaves);
+  uint32_t* mask_s = reinterpret_cast<uint32_t*>(lds + off_flag + nflag);
   short* idx_s = reinterpret_cast<short*>(mask_s + W);
-  float* xo_s = reinterpret_cast<float*>(
-      lds + ((off_flag + nchunk * kDecWaves + W * 4 + K * 2 + 15) & ~15));
+  float* xo_s = reinterpret_cast<float*>(lds + ((off_flag + nflag + W * 4 + K * 2 + 15) & ~15));
   float* wo_s = xo_s + kOutChunk * 16;
   // 8 bytes per lane that absorb the stores of chunks past K (branch-free stores)
   int8_t* sink_s = reinterpret_cast<int8_t*>(wo_s + kOutChunk * 16);
@@ -74,22 +118,20 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int n0 = blockIdx.x * 16;
 
   // 1. activations into registers (issued first: waiting for them then leaves every
-  // weight load in flight). Every block reads all of X, so each block walks its
-  // chunks from a different starting group: register j holds chunk group
-  // (j + xrot) mod CL, and concurrent blocks of one XCD (block ids 8 apart) hit
-  // different L2 channels instead of all requesting the same lines at once.
-  const int xrot = (blockIdx.x >> 3) & (CL - 1);
-  v8h xv[RW][CL];
+  // weight load in flight). Every block reads all of X; the chunk groups of its waves
+  // are rotated per block so that concurrent blocks of one XCD (block ids 8 apart)
+  // start on different L2 channels. Rows past M and chunks past K read the last valid
+  // row or chunk: repeats change neither a maximum nor an OR, and their codes go to
+  // the sink.
+  const int xrot = (blockIdx.x >> 3) & 7;
+  const int cbase = 64 * ((wave + xrot) & 7) + lane;
+  v8h xv[MR][CC];
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int m = wave + kDecWaves * i;
+  for (int j = 0; j < CC; ++j) {
+    const int c = min(cbase + 512 * j, nchunk - 1);
 #pragma unroll
-    for (int j = 0; j < CL; ++j) {
-      const int c = lane + 64 * ((j + xrot) & (CL - 1));
-      const v8h v = *reinterpret_cast<const v8h*>(a.X + static_cast<size_t>(min(m, M - 1)) * K +
-                                                  min(c, nchunk - 1) * 8);
-      xv[i][j] = (m < M && c < nchunk) ? v : v8h{};
-    }
+    for (int m = 0; m < MR; ++m)
+      xv[m][j] = *reinterpret_cast<const v8h*>(a.X + static_cast<size_t>(min(m, M - 1)) * K + c * 8);
   }
   // 2. the weight stream. Wq is unit-tiled: the block's 16 rows are one contiguous run
   // of KS units, and unit s is exactly the 16 x 64 A operand of k-step s, so each load
@@ -119,129 +161,136 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   // the epilogue's column constant, loaded now so that its latency hides under the rest
   const float aw_pre = a.a_w[n0 + (tid & 15)];
 
-  // 3. outlier flags ("LLM.int8()", Mixed-precision decomposition: a feature column is
-  // an outlier when any of its values reaches the threshold). Magnitudes as fp16 bits:
-  // mag[i][j][d] holds two halves; the per-chunk max over this wave's rows decides
-  // whether the exact per-column test is needed. Each wave writes one flag byte per
-  // chunk (no zeroing, no atomics); the OR over waves is taken after the barrier.
-  const unsigned tb = threshold_bits(a.t);
+  // 3. outlier columns ("LLM.int8()", Mixed-precision decomposition: a feature column is
+  // an outlier when any of its values reaches the threshold). Magnitudes as fp16 bits,
+  // two per dword: the largest over the rows, compared with the threshold bits, gives
+  // a keep-mask per half (0 on outlier columns) and one byte of outlier bits per chunk.
+  const unsigned tb = threshold_bits(a.t), tb2 = tb * 0x10001u;
+  v4u keep[CC];
 #pragma unroll
-  for (int j = 0; j < CL; ++j) {
-    const int c = lane + 64 * ((j + xrot) & (CL - 1));
-    unsigned f = 0;
+  for (int j = 0; j < CC; ++j) {
+    const int c = cbase + 512 * j;
+    v4u cm = __builtin_bit_cast(v4u, xv[0][j]) & 0x7fff7fffu;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      unsigned cm = 0;
+    for (int m = 1; m < MR; ++m)
 #pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        const unsigned mg = __builtin_bit_cast(v4u, xv[i][j])[d] & 0x7fff7fffu;
-        cm = i == 0 ? mg : pk_max_u16(cm, mg);
-      }
-      f |= static_cast<unsigned>((cm & 0xffffu) >= tb) << (2 * d);
-      f |= static_cast<unsigned>((cm >> 16) >= tb) << (2 * d + 1);
-    }
-    *(c < nchunk ? reinterpret_cast<unsigned char*>(flag_s + c * kDecWaves + wave)
-                 : reinterpret_cast<unsigned char*>(sink_s + lane)) = static_cast<unsigned char>(f);
+      for (int d = 0; d < 4; ++d)
+        cm[d] = pk_max_u16(cm[d], __builtin_bit_cast(v4u, xv[m][j])[d] & 0x7fff7fffu);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) keep[j][d] = keep_halves(cm[d], tb2);
+    // one byte of each half's keep-mask (halves 0-3, then 4-7), a different bit taken
+    // from each byte, summed: bit e is set where column 8 c + e is kept
+    const unsigned p = __builtin_amdgcn_perm(keep[j][1], keep[j][0], 0x06040200u);
+    const unsigned q = __builtin_amdgcn_perm(keep[j][3], keep[j][2], 0x06040200u);
+    const unsigned kb = __builtin_amdgcn_sad_u8((p & 0x08040201u) | (q & 0x80402010u), 0u, 0u);
+    *(c < nchunk ? flag_s + c : reinterpret_cast<unsigned char*>(sink_s + lane)) =
+        static_cast<unsigned char>(~kb);
   }
+
+  // 4. row absmax over the kept columns ("LLM.int8()", Vector-wise quantization: one
+  // constant per row of X): this thread's maximum of each row, then the wave's (the
+  // rows' DPP reductions are independent, so their steps interleave), then (after the
+  // barrier) the block's
+  unsigned rmx[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    unsigned v = 0;
+#pragma unroll
+    for (int j = 0; j < CC; ++j)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        v = pk_max_u16(v, __builtin_bit_cast(v4u, xv[m][j])[d] & 0x7fff7fffu & keep[j][d]);
+    rmx[m] = max(v & 0xffffu, v >> 16);
+  }
+  wave_max_u32_n<MR>(rmx);
+  if (lane == 0)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) rmax_w[wave][m] = rmx[m];
   lds_barrier();
 
-  // 4. combined flags of the owned chunks; outlier values are zeroed in the registers
-  // (their codes are 0 and they do not enter the row constant), branch-free: bit e of
-  // the chunk's flags clears half e through a keep-mask per dword
+  // 5. row constants: lane r of every wave combines row r's maxima over the waves and
+  // takes its quantization bracket; the rows' values are read from those lanes below
+  float am_l;
+  QuantBracket br_l;
+  {
+    const int r = min(lane, MR - 1);
+    unsigned v = 0;
 #pragma unroll
-  for (int j = 0; j < CL; ++j) {
-    const int c = lane + 64 * ((j + xrot) & (CL - 1));
-    const v2u fw = *reinterpret_cast<const v2u*>(flag_s + min(c, nchunk - 1) * kDecWaves);
-    const unsigned o = fw[0] | fw[1];
-    const unsigned keep = c < nchunk ? ~(o | (o >> 8) | (o >> 16) | (o >> 24)) : ~0u;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const unsigned km = ((keep >> (2 * d)) & 1u ? 0x0000ffffu : 0u) |
-                          ((keep >> (2 * d + 1)) & 1u ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        v4u u = __builtin_bit_cast(v4u, xv[i][j]);
-        u[d] &= km;
-        xv[i][j] = __builtin_bit_cast(v8h, u);
-      }
-    }
+    for (int w = 0; w < kDecWaves; ++w) v = max(v, rmax_w[w][r]);
+    am_l = half_bits_to_float(v);
+    br_l = quant_bracket(am_l);
   }
-  // 5. mask words and their ranks: thread t < W owns word t (chunks 4t .. 4t + 3)
+  if (wave == 0 && lane < M) rowmax_s[lane] = am_l;
+
+  // 6. mask words and their ranks: thread t < W owns word t (chunks 4t .. 4t + 3, whose
+  // outlier bytes are its little-endian bytes)
   int mine = 0;
   if (tid < W) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = 4 * tid + q;
-      if (c < nchunk) {
-        const v2u fw = *reinterpret_cast<const v2u*>(flag_s + c * kDecWaves);
-        const unsigned o = fw[0] | fw[1];
-        word |= ((o | (o >> 8) | (o >> 16) | (o >> 24)) & 0xffu) << (8 * q);
-      }
-    }
+    uint32_t word = *reinterpret_cast<const uint32_t*>(flag_s + 4 * tid);
+    const int valid = nchunk - 4 * tid;  // chunks of this word inside K (>= 1)
+    if (valid < 4) word &= (1u << (8 * valid)) - 1u;
     mask_s[tid] = word;
     mine = __popc(word);
   }
   const int incl = wave_prefix_sum(mine);
   if (lane == 63) wave_tot[wave] = incl;
 
-  // 6. row absmax over the kept columns ("LLM.int8()", Vector-wise quantization: one
-  // constant per row of X) and the row's codes into LDS
+  // 7. codes into LDS, outlier columns cleared first (their codes are 0). The bracketing
+  // pair (see quant8_bracket) decides; (row, chunk) slots where it disagrees (values at
+  // or within about 2^-15 of a half-integer) are rewritten with quant8_exact below.
+  unsigned redo = 0;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int m = wave + kDecWaves * i;
-    if (m >= M) break;  // wave-uniform
-    unsigned pm = 0;
+  for (int m = 0; m < MR; ++m) {
+    if (m >= M) break;  // block-uniform
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.hi), m));
 #pragma unroll
-    for (int j = 0; j < CL; ++j)
+    for (int j = 0; j < CC; ++j) {
+      const int c = cbase + 512 * j;
+      v4u u = __builtin_bit_cast(v4u, xv[m][j]);
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        pm = pk_max_u16(pm, __builtin_bit_cast(v4u, xv[i][j])[d] & 0x7fff7fffu);
-    const unsigned mb = wave_max_u32(max(pm & 0xffffu, pm >> 16));
-    const float am = half_bits_to_float(mb);
-    const QuantBracket br = quant_bracket(am);
-    if (lane == 0) rowmax_s[m] = am;
-    // codes from the bracketing pair (see quant8_bracket); chunks where the pair
-    // disagrees (values at or within about 2^-15 of a half-integer) are rewritten
-    // with quant8_exact after the loop, behind one wave-uniform test
-    unsigned redo = 0;
-#pragma unroll
-    for (int j = 0; j < CL; ++j) {
-      const int c = lane + 64 * ((j + xrot) & (CL - 1));
+      for (int d = 0; d < 4; ++d) u[d] &= keep[j][d];
+      xv[m][j] = __builtin_bit_cast(v8h, u);
       unsigned b1[8], b2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float xf = static_cast<float>(xv[i][j][e]);
-        b1[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.lo, kRoundMagic));
-        b2[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.hi, kRoundMagic));
+        const float xf = static_cast<float>(xv[m][j][e]);
+        b1[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, lo, kRoundMagic));
+        b2[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, hi, kRoundMagic));
       }
       v2u o;
       o[0] = pack_low_bytes(b1[0], b1[1], b1[2], b1[3]);
       o[1] = pack_low_bytes(b1[4], b1[5], b1[6], b1[7]);
       const unsigned dis = (o[0] ^ pack_low_bytes(b2[0], b2[1], b2[2], b2[3])) |
                            (o[1] ^ pack_low_bytes(b2[4], b2[5], b2[6], b2[7]));
-      redo |= dis != 0u ? 1u << j : 0u;
+      redo |= dis != 0u ? 1u << (m * CC + j) : 0u;
       *reinterpret_cast<v2u*>(c < nchunk ? xq_s + m * xs + c * 8 : sink_s + lane * 8) = o;
     }
-    // One pass of a do-while always runs, so its code is fetched in order on every
-    // launch (a rarely taken branch into cold code costs microseconds here): each lane
-    // selects its lowest pending chunk (or none) and rewrites it with quant8_exact.
-    unsigned pend = redo;
-    do {
-      const unsigned jb = __builtin_ctz(pend | (1u << CL));  // CL: nothing pending
-      v8h xs8 = v8h{};
-      int cs = 0;
-#pragma unroll
-      for (int j = 0; j < CL; ++j) {
-        const bool hit = jb == static_cast<unsigned>(j);
-        xs8 = hit ? xv[i][j] : xs8;
-        cs = hit ? lane + 64 * ((j + xrot) & (CL - 1)) : cs;
-      }
-      const v2u o = quant8_exact(xs8, am, br.lo);
-      *reinterpret_cast<v2u*>(jb < CL && cs < nchunk ? xq_s + m * xs + cs * 8 : sink_s + lane * 8) = o;
-      pend &= pend - 1u;
-    } while (__ballot(pend != 0u) != 0);
   }
+  // One pass of a do-while always runs, so its code is fetched in order on every
+  // launch (a rarely taken branch into cold code costs microseconds here): each lane
+  // selects its lowest pending slot (or none) and rewrites it with quant8_exact, its
+  // row's constant and bracket read from the lane that holds them.
+  unsigned pend = redo;
+  do {
+    const unsigned jb = __builtin_ctz(pend | (1u << (MR * CC)));  // MR * CC: nothing pending
+    v8h xs8 = v8h{};
+    int ms = 0, cs = 0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        const bool hit = jb == static_cast<unsigned>(m * CC + j);
+        xs8 = hit ? xv[m][j] : xs8;
+        ms = hit ? m : ms;
+        cs = hit ? cbase + 512 * j : cs;
+      }
+    const float am = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, am_l)));
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, br_l.lo)));
+    const v2u o = quant8_exact(xs8, am, lo);
+    *reinterpret_cast<v2u*>(jb < MR * CC && cs < nchunk ? xq_s + ms * xs + cs * 8 : sink_s + lane * 8) = o;
+    pend &= pend - 1u;
+  } while (__ballot(pend != 0u) != 0);
   lds_barrier();
   int before = incl - mine;
   for (int i = 0; i < wave; ++i) before += wave_tot[i];
@@ -267,7 +316,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int pw = a.Wq[unit_offset(n0 + pq, pcol, ks)];
   const _Float16 px = a.X[static_cast<size_t>(min(pq, M - 1)) * K + pcol];
 
-  // 7. int8 MFMA: D[n_local][m] += Wq[n0 + n_local, k] * Xq[m, k]; the Xq fragments
+  // 8. int8 MFMA: D[n_local][m] += Wq[n0 + n_local, k] * Xq[m, k]; the Xq fragments
   // are read (at clamped addresses, discarded past M or K) before the MFMA chain
   // (in batches of at most 8 steps, to bound the registers the fragments take)
   const int mtok = lane & 15;
@@ -294,7 +343,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   xo_s[pr * 16 + pq] = pr < npre && pq < M ? static_cast<float>(px) : 0.0f;
   lds_barrier();
 
-  // 8. epilogue: thread t < 256 -> (token m, output feature n0 + nl). The int32
+  // 9. epilogue: thread t < 256 -> (token m, output feature n0 + nl). The int32
   // partials of the waves are summed exactly; the outlier columns' product is taken
   // in fp32 from the exact fp16 X and the int8 weight dequantized by a_w / 127.
   float yo = 0.0f;
@@ -334,18 +383,20 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int W = (a.K + 31) / 32, nchunk = a.K / 8;
   const size_t off_flag = (static_cast<size_t>(a.M) * (a.K + 16) + 15) & ~size_t(15);
-  const size_t head = off_flag + static_cast<size_t>(nchunk) * kDecWaves + W * 4 +
+  const size_t head = off_flag + static_cast<size_t>((nchunk + 3) & ~3) + W * 4 +
                       static_cast<size_t>(a.K) * 2;
   const size_t lds = ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 8;
-  const int rw = rows_per_wave(a.M), cl = chunks_per_lane(a.K);
+  const int mr = rows_held(a.M), spw = steps_per_wave(a.K);
   const dim3 grid(a.N / 16), block(kDecThreads);
-#define I8MM_DEC(R, C)                                                              \
-  if (rw == R && cl == C) {                                                         \
-    hipLaunchKernelGGL((k_decode<R, C>), grid, block, lds, s, a);                   \
+#define I8MM_DEC(R, P)                                                              \
+  if (mr == R && spw == P) {                                                        \
+    hipLaunchKernelGGL((k_decode<R, P>), grid, block, lds, s, a);                   \
     return hipGetLastError();                                                       \
   }
-  I8MM_DEC(1, 1) I8MM_DEC(1, 2) I8MM_DEC(1, 4) I8MM_DEC(1, 8) I8MM_DEC(1, 16)
-  I8MM_DEC(2, 1) I8MM_DEC(2, 2) I8MM_DEC(2, 4) I8MM_DEC(2, 8)
+  I8MM_DEC(2, 2) I8MM_DEC(2, 4) I8MM_DEC(2, 8) I8MM_DEC(2, 16)
+  I8MM_DEC(4, 2) I8MM_DEC(4, 4) I8MM_DEC(4, 8) I8MM_DEC(4, 16)
+  I8MM_DEC(8, 2) I8MM_DEC(8, 4) I8MM_DEC(8, 8) I8MM_DEC(8, 16)
+  I8MM_DEC(16, 2) I8MM_DEC(16, 4) I8MM_DEC(16, 8)
 #undef I8MM_DEC
   return hipErrorInvalidValue;
 }
