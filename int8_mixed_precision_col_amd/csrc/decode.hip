@@ -3,17 +3,21 @@
 // "What is 8-bit LLM quantization?", Does INT8 always improve speed?: for the decoding
 // workload the gain comes from the smaller weights cutting memory traffic. With
 // M <= 16 tokens the int8 weight stream (N x K bytes) is the whole cost, so one
-// launch does every step and reads each Wq byte from HBM exactly once:
-//   1. each block issues the loads of its 16 Wq rows (all K) into registers first;
-//   2. while they are in flight it reads all of X (small, L2-resident): wave w owns
-//      rows w, w+4, ..., lane l owns the 8-column chunks l, l+64, ...; it finds the
-//      outlier columns (|X| >= t in any row), ranks them, takes each row's absmax over
-//      the other columns and writes Xq into LDS. Every block repeats this for the
-//      whole of X, which costs L2 reads and VALU time but no second launch and no
-//      grid-wide wait;
+// launch does every step and reads each Wq byte from HBM exactly once. One block of
+// 8 waves per 16 output features:
+//   1. each thread loads its 8-column chunks of X for every token row, then issues its
+//      wave's share of the block's 16 Wq rows (whole 1 KB units) into registers;
+//   2. while the weights are in flight: per chunk, the largest magnitude over the
+//      rows against the threshold gives the outlier columns (a keep-mask per column,
+//      one byte of outlier bits per chunk in LDS); per row, the absmax over the kept
+//      columns, reduced over the wave with DPP and over the block through LDS; the
+//      rows' brackets of 127 / a_x; the codes of every (row, chunk) into LDS, with an
+//      exact pass for the rare values where the bracket cannot decide; the outlier
+//      columns' ranks. Every block repeats this for the whole of X, which costs L2
+//      reads and VALU time but no second launch and no grid-wide wait;
 //   3. v_mfma_i32_16x16x64_i8 with Wq rows as the 16-row operand and Xq rows as the
-//      16-column operand (tokens past M are zero), K split over the 4 waves;
-//   4. the four int32 partials are summed exactly through LDS; the epilogue applies
+//      16-column operand (tokens past M are zero), K split over the 8 waves;
+//   4. the eight int32 partials are summed exactly through LDS; the epilogue applies
 //      the outer-product dequant and adds the outlier columns' product in fp32
 //      (exact fp16 X times the int8 weight dequantized by a_w / 127, both staged in
 //      LDS) before the single rounding to fp16.
@@ -102,16 +106,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int K = a.K, M = a.M;
   const int W = (K + 31) / 32, nchunk = K / 8, xs = K + 16;
   const int nflag = (nchunk + 3) & ~3;
-  // LDS: Xq [M][K + 16] | outlier bits, one byte per chunk [nflag] | mask words [W] |
-  // outlier column list [K] (short) | outlier staging | sink
-  int8_t* xq_s = reinterpret_cast<int8_t*>(lds);
-  const int off_flag = (M * xs + 15) & ~15;
+  // LDS: X with its outlier columns cleared [M][K] | Xq [M][K + 16] | outlier bits, one
+  // byte per chunk [nflag] | mask words [W] | outlier column list [K] (short) | outlier
+  // staging | sink
+  _Float16* x_s = reinterpret_cast<_Float16*>(lds);
+  const int off_xq = M * K * 2;
+  int8_t* xq_s = reinterpret_cast<int8_t*>(lds + off_xq);
+  const int off_flag = off_xq + ((M * xs + 15) & ~15);
   unsigned char* flag_s = reinterpret_cast<unsigned char*>(lds + off_flag);
   uint32_t* mask_s = reinterpret_cast<uint32_t*>(lds + off_flag + nflag);
   short* idx_s = reinterpret_cast<short*>(mask_s + W);
   float* xo_s = reinterpret_cast<float*>(lds + ((off_flag + nflag + W * 4 + K * 2 + 15) & ~15));
   float* wo_s = xo_s + kOutChunk * 16;
-  // 8 bytes per lane that absorb the stores of chunks past K (branch-free stores)
+  // 16 bytes per lane that absorb the stores of chunks past K (branch-free stores)
   int8_t* sink_s = reinterpret_cast<int8_t*>(wo_s + kOutChunk * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -251,6 +258,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) u[d] &= keep[j][d];
       xv[m][j] = __builtin_bit_cast(v8h, u);
+      *reinterpret_cast<v8h*>(c < nchunk ? reinterpret_cast<char*>(x_s + m * K + c * 8)
+                                         : reinterpret_cast<char*>(sink_s + lane * 16)) = xv[m][j];
       unsigned b1[8], b2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -263,33 +272,49 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       o[1] = pack_low_bytes(b1[4], b1[5], b1[6], b1[7]);
       const unsigned dis = (o[0] ^ pack_low_bytes(b2[0], b2[1], b2[2], b2[3])) |
                            (o[1] ^ pack_low_bytes(b2[4], b2[5], b2[6], b2[7]));
-      redo |= dis != 0u ? 1u << (m * CC + j) : 0u;
+      redo |= dis != 0u && c < nchunk ? 1u << (m * CC + j) : 0u;
       *reinterpret_cast<v2u*>(c < nchunk ? xq_s + m * xs + c * 8 : sink_s + lane * 8) = o;
     }
   }
-  // One pass of a do-while always runs, so its code is fetched in order on every
-  // launch (a rarely taken branch into cold code costs microseconds here): each lane
-  // selects its lowest pending slot (or none) and rewrites it with quant8_exact, its
-  // row's constant and bracket read from the lane that holds them.
-  unsigned pend = redo;
+  // Exact codes where the pair disagreed, one element per lane per pass. One pass of the
+  // loop always runs, so its code is fetched in order on every launch (a rarely taken
+  // branch into cold code costs microseconds here). A pass takes the lane's lowest
+  // pending slot, reads that chunk back from LDS (this lane wrote it), redoes the pair
+  // to find the elements that differ, and settles the lowest one not yet settled with
+  // the exact comparison of quant8_exact, patching its code byte.
+  unsigned pend = redo, done = 0;
   do {
     const unsigned jb = __builtin_ctz(pend | (1u << (MR * CC)));  // MR * CC: nothing pending
-    v8h xs8 = v8h{};
-    int ms = 0, cs = 0;
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int j = 0; j < CC; ++j) {
-        const bool hit = jb == static_cast<unsigned>(m * CC + j);
-        xs8 = hit ? xv[m][j] : xs8;
-        ms = hit ? m : ms;
-        cs = hit ? cbase + 512 * j : cs;
-      }
+    const bool any = jb < static_cast<unsigned>(MR * CC);
+    const int ms = any ? static_cast<int>(jb) / CC : 0;
+    const int cs = cbase + 512 * (any ? static_cast<int>(jb) % CC : 0);
+    const v8h x = *reinterpret_cast<const v8h*>(x_s + (any ? ms * K + cs * 8 : 0));
     const float am = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, am_l)));
     const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, br_l.lo)));
-    const v2u o = quant8_exact(xs8, am, lo);
-    *reinterpret_cast<v2u*>(jb < MR * CC && cs < nchunk ? xq_s + ms * xs + cs * 8 : sink_s + lane * 8) = o;
-    pend &= pend - 1u;
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, br_l.hi)));
+    unsigned diff = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xf = static_cast<float>(x[e]);
+      const unsigned t1 = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, lo, kRoundMagic));
+      const unsigned t2 = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, hi, kRoundMagic));
+      diff |= t1 != t2 ? 1u << e : 0u;
+    }
+    diff &= ~done;
+    const int e = __builtin_ctz(diff | 0x100u);  // 8: nothing left in this slot
+    const unsigned xd = __builtin_bit_cast(v4u, x)[(e >> 1) & 3];
+    const float xf = half_bits_to_float((e & 1) ? xd >> 16 : xd & 0xffffu);
+    const float w = fabsf(xf);
+    const float q1 = __builtin_fmaf(w, lo, kRoundMagic) - kRoundMagic;
+    const float d = __builtin_fmaf(2.0f * q1 + 1.0f, am, -254.0f * w);
+    const int qi = static_cast<int>(q1);
+    const int q = qi + ((d < 0.0f || (d == 0.0f && (qi & 1))) ? 1 : 0);
+    const bool ok = any && e < 8;
+    *(ok ? xq_s + ms * xs + cs * 8 + e : sink_s + lane * 16) =
+        static_cast<int8_t>(xf < 0.0f ? -q : q);
+    const bool slot_done = (diff & (diff - 1u)) == 0u;  // e was the last one (or none)
+    done = slot_done ? 0u : done | (1u << e);
+    pend = slot_done ? pend & (pend - 1u) : pend;
   } while (__ballot(pend != 0u) != 0);
   lds_barrier();
   int before = incl - mine;
@@ -382,10 +407,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int W = (a.K + 31) / 32, nchunk = a.K / 8;
-  const size_t off_flag = (static_cast<size_t>(a.M) * (a.K + 16) + 15) & ~size_t(15);
+  const size_t off_flag = static_cast<size_t>(a.M) * a.K * 2 +
+                          ((static_cast<size_t>(a.M) * (a.K + 16) + 15) & ~size_t(15));
   const size_t head = off_flag + static_cast<size_t>((nchunk + 3) & ~3) + W * 4 +
                       static_cast<size_t>(a.K) * 2;
-  const size_t lds = ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 8;
+  const size_t lds = ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 16;
   const int mr = rows_held(a.M), spw = steps_per_wave(a.K);
   const dim3 grid(a.N / 16), block(kDecThreads);
 #define I8MM_DEC(R, P)                                                              \

@@ -87,6 +87,49 @@ def test_quant_rows_adversarial():
     assert 10 in ref["idx"] and 11 not in ref["idx"] and ref["a_x"][3] == 0
 
 
+def tie_rows(seed, M, K):
+    """Rows whose codes are exact half-integers in bulk. With row absmax a = 127 / 2^p,
+    127 x / a = 2^p x, so every x = (k + 1/2) / 2^p (exact in fp16) is a tie that
+    round-half-to-even must settle; the bracketing pair disagrees on all of them. Row 0
+    is ties only (max 127/64), row 1 half ties, row 2 ties under a = 127/32, row 3 also
+    holds an outlier column; the other rows are ordinary."""
+    rng = np.random.default_rng([seed, 11])
+    X = (rng.standard_normal((M, K)) * 0.5).astype(np.float32)
+    sgn = rng.choice([-1.0, 1.0], size=(M, K))
+    ties64 = (rng.integers(0, 127, size=(M, K)) + 0.5) / 64.0 * sgn
+    ties32 = (rng.integers(0, 127, size=(M, K)) + 0.5) / 32.0 * sgn
+    X[0] = ties64[0]
+    X[0, 5] = 127.0 / 64.0
+    if M > 1:
+        half = rng.random(K) < 0.5
+        X[1] = np.where(half, ties64[1], np.clip(X[1], -1.9, 1.9))
+        X[1, 9] = -127.0 / 64.0
+    if M > 2:
+        X[2] = ties32[2]
+        X[2, 3] = 127.0 / 32.0
+    if M > 3:
+        X[3] = ties64[3]
+        X[3, 1] = 127.0 / 64.0
+        X[3, 7] = 6.0                      # outlier column: excluded from the row max
+    return X.astype(np.float16)
+
+
+@pytest.mark.parametrize("M,K", [(8, 1024), (8, 4096), (3, 8192), (40, 1040)])
+def test_ties_in_bulk(M, K):
+    """Codes at exact half-integers, many per 8-column chunk, on both paths: the int32
+    sums (and, on the multi-kernel path, Xq itself) must match the oracle bit for bit."""
+    path = "decode" if binding.is_decode(M, K) else "prefill"
+    announce(f"ties in bulk {path} M={M} K={K}")
+    X = tie_rows(M + K, M, K)
+    if path == "prefill":
+        _quant_case(X, 6.0, 16)
+    W = weight(M + 2 * K, K, 272)
+    ref, Y, acc = _mixed(X, W, 6.0, mo=16)
+    assert ref["a_x"][0] == np.float32(127.0 / 64.0) and (M <= 3 or ref["count"] >= 1)
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
 # ------------------------------------------------------------------ mixed matmul
 
 def _mixed(X, W, t, mo=256, workspace=None):
