@@ -100,23 +100,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   constexpr int CC = SPW > 8 ? 2 : 1;  // chunks per thread: K <= 4096 needs one
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int red[kDecWaves][16][17];
-  __shared__ int wave_tot[kDecWaves];
+  __shared__ int count_s;
   __shared__ unsigned rmax_w[kDecWaves][MR];  // each wave's row maxima (fp16 bits)
   __shared__ float rowmax_s[kDecMaxM];
   const int K = a.K, M = a.M;
   const int W = (K + 31) / 32, nchunk = K / 8, xs = K + 16;
   const int nflag = (nchunk + 3) & ~3;
   // LDS: X with its outlier columns cleared [M][K] | Xq [M][K + 16] | outlier bits, one
-  // byte per chunk [nflag] | mask words [W] | outlier column list [K] (short) | outlier
-  // staging | sink
+  // byte per chunk [nflag] | outlier column list [K] (short) | outlier staging | sink
   _Float16* x_s = reinterpret_cast<_Float16*>(lds);
   const int off_xq = M * K * 2;
   int8_t* xq_s = reinterpret_cast<int8_t*>(lds + off_xq);
   const int off_flag = off_xq + ((M * xs + 15) & ~15);
   unsigned char* flag_s = reinterpret_cast<unsigned char*>(lds + off_flag);
-  uint32_t* mask_s = reinterpret_cast<uint32_t*>(lds + off_flag + nflag);
-  short* idx_s = reinterpret_cast<short*>(mask_s + W);
-  float* xo_s = reinterpret_cast<float*>(lds + ((off_flag + nflag + W * 4 + K * 2 + 15) & ~15));
+  short* idx_s = reinterpret_cast<short*>(lds + off_flag + nflag);
+  float* xo_s = reinterpret_cast<float*>(lds + ((off_flag + nflag + K * 2 + 15) & ~15));
   float* wo_s = xo_s + kOutChunk * 16;
   // 16 bytes per lane that absorb the stores of chunks past K (branch-free stores)
   int8_t* sink_s = reinterpret_cast<int8_t*>(wo_s + kOutChunk * 16);
@@ -229,18 +227,38 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   }
   if (wave == 0 && lane < M) rowmax_s[lane] = am_l;
 
-  // 6. mask words and their ranks: thread t < W owns word t (chunks 4t .. 4t + 3, whose
-  // outlier bytes are its little-endian bytes)
-  int mine = 0;
-  if (tid < W) {
-    uint32_t word = *reinterpret_cast<const uint32_t*>(flag_s + 4 * tid);
-    const int valid = nchunk - 4 * tid;  // chunks of this word inside K (>= 1)
-    if (valid < 4) word &= (1u << (8 * valid)) - 1u;
-    mask_s[tid] = word;
-    mine = __popc(word);
+  // 6. the outlier column list, ascending: wave 0, lane l takes the mask words
+  // 4l .. 4l + 3 (W <= 256), whose little-endian bytes are the outlier bytes of chunks
+  // 16l .. 16l + 15; a prefix sum over the lanes gives each word's first rank
+  if (wave == 0) {
+    const v4u f = *reinterpret_cast<const v4u*>(flag_s + 16 * min(lane, (W - 1) >> 2));
+    unsigned wd[4];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 4 * lane + q, valid = nchunk - 4 * t;  // chunks of word t inside K
+      wd[q] = t >= W ? 0u : valid >= 4 ? f[q] : f[q] & ((1u << (8 * valid)) - 1u);
+      cnt += __popc(wd[q]);
+    }
+    const int incl = wave_prefix_sum(cnt);
+    int r = incl - cnt;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      for (unsigned bits = wd[q]; bits; bits &= bits - 1u)
+        idx_s[r++] = static_cast<short>((4 * lane + q) * 32 + __builtin_ctz(bits));
+    if (lane == 63) count_s = incl;
   }
-  const int incl = wave_prefix_sum(mine);
-  if (lane == 63) wave_tot[wave] = incl;
+  lds_barrier();
+  const int count = count_s;
+  // The values of the first kPre outlier columns (one (column, row) pair per thread)
+  // are loaded now, so that their latency hides under the quantization and the MFMA
+  // (unconditional loads at a valid column, discarded past the count); they go to LDS
+  // with the partials.
+  const int npre = min(count, kPre);
+  const int pr = tid >> 4, pq = tid & 15;
+  const int pcol = pr < npre ? idx_s[pr] : 0;
+  const int pw = a.Wq[unit_offset(n0 + pq, pcol, ks)];
+  const _Float16 px = a.X[static_cast<size_t>(min(pq, M - 1)) * K + pcol];
 
   // 7. codes into LDS, outlier columns cleared first (their codes are 0). The bracketing
   // pair (see quant8_bracket) decides; (row, chunk) slots where it disagrees (values at
@@ -317,29 +335,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     pend = slot_done ? pend & (pend - 1u) : pend;
   } while (__ballot(pend != 0u) != 0);
   lds_barrier();
-  int before = incl - mine;
-  for (int i = 0; i < wave; ++i) before += wave_tot[i];
-  int count = 0;
-#pragma unroll
-  for (int i = 0; i < kDecWaves; ++i) count += wave_tot[i];
-  if (tid < W) {
-    uint32_t bits = mask_s[tid];
-    for (int r = before; bits; ++r) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      idx_s[r] = static_cast<short>(tid * 32 + b);
-    }
-  }
-  lds_barrier();
-  // The values of the first kPre outlier columns (one (column, row) pair per thread)
-  // are loaded now, so that their latency overlaps the MFMA (unconditional loads at a
-  // valid column, discarded past the count); they go to LDS with the partials.
   const int m = (tid >> 4) & 15, nl = tid & 15, n = n0 + nl;
-  const int npre = min(count, kPre);
-  const int pr = tid >> 4, pq = tid & 15;
-  const int pcol = pr < npre ? idx_s[pr] : 0;
-  const int pw = a.Wq[unit_offset(n0 + pq, pcol, ks)];
-  const _Float16 px = a.X[static_cast<size_t>(min(pq, M - 1)) * K + pcol];
 
   // 8. int8 MFMA: D[n_local][m] += Wq[n0 + n_local, k] * Xq[m, k]; the Xq fragments
   // are read (at clamped addresses, discarded past M or K) before the MFMA chain
@@ -406,10 +402,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const int W = (a.K + 31) / 32, nchunk = a.K / 8;
+  const int nchunk = a.K / 8;
   const size_t off_flag = static_cast<size_t>(a.M) * a.K * 2 +
                           ((static_cast<size_t>(a.M) * (a.K + 16) + 15) & ~size_t(15));
-  const size_t head = off_flag + static_cast<size_t>((nchunk + 3) & ~3) + W * 4 +
+  const size_t head = off_flag + static_cast<size_t>((nchunk + 3) & ~3) +
                       static_cast<size_t>(a.K) * 2;
   const size_t lds = ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 16;
   const int mr = rows_held(a.M), spw = steps_per_wave(a.K);
