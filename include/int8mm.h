@@ -167,8 +167,8 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
  * LLM.int8()?: 8-bit weight storage does not make every activation or operation
  * int8; Does INT8 always improve speed?: the decoding workload gains from the
  * smaller weight stream). The comparison point for the decode path above.
- *   X, M, K       fp16 activations [M, K], 1 <= M <= 16 and M (K + 8) <= 65536
- *                 (X is staged whole in on-chip memory).
+ *   X, M, K       fp16 activations [M, K], 1 <= M <= 16 and M K < 2^30 (X is
+ *                 read through a buffer resource, whose byte offsets are 31-bit).
  *   Wq, w_absmax  unit-tiled int8 weight and fp32 [N] from int8_prepare_weight.
  *   Y             out, fp16 [M, N] row-major.
  * Sums: the products of fp16 X and the int8 codes are exact in fp32 and accumulate
