@@ -52,31 +52,6 @@ __device__ __forceinline__ unsigned pack4(int a, int b, int c, int d) {
          ((static_cast<unsigned>(c) & 0xFFu) << 16) | (static_cast<unsigned>(d) << 24);
 }
 
-// Codes of 8 halves under absmax a (r = quant_scale(a)); elements whose bit is set in
-// drop (outlier columns) get code 0. Same decision as quant_code_fast, with one
-// near-tie branch per 8 elements instead of one per element.
-__device__ __forceinline__ v2u quant8(const v8h& v, unsigned drop, float a, float r) {
-  float q[8];
-  bool near = false;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float t = static_cast<float>(v[e]) * r;
-    q[e] = __builtin_rintf(t);
-    near |= fabsf(t - q[e]) > 0.5f - 0x1p-15f;
-  }
-  if (__builtin_expect(near, 0)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = static_cast<float>(quant_code(v[e], a));
-  }
-  int c[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = ((drop >> e) & 1u) ? 0 : static_cast<int>(q[e]);
-  v2u o;
-  o[0] = pack4(c[0], c[1], c[2], c[3]);
-  o[1] = pack4(c[4], c[5], c[6], c[7]);
-  return o;
-}
-
 // fp32 1.5 * 2^23. For |p| < 2^22, the fused fma(x, r, kRoundMagic) rounds the exact
 // product p = x r to an integer (half-even, in the adder) and leaves that integer, as
 // kRoundMagic + q, in the result's low bits: its low byte is q as an int8.
@@ -102,35 +77,7 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned b0, unsigned b1, uns
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Codes of 8 halves under absmax a, with br = quant_bracket(a): quant_code of each.
-// p_lo = x br.lo and p_hi = x br.hi bracket the exact 127 x / a, and round-half-even
-// is monotonic, so where both round to the same integer that integer is the exact
-// code; only 8-element groups holding a disagreement (a value within about 2^-15 of a
-// half-integer) take the correctly rounded divide.
-__device__ __forceinline__ v2u quant8_bracket(const v8h& x, float a, QuantBracket br) {
-  unsigned b1[8], b2[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float xf = static_cast<float>(x[e]);
-    b1[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.lo, kRoundMagic));
-    b2[e] = __builtin_bit_cast(unsigned, __builtin_fmaf(xf, br.hi, kRoundMagic));
-  }
-  v2u o;
-  o[0] = pack_low_bytes(b1[0], b1[1], b1[2], b1[3]);
-  o[1] = pack_low_bytes(b1[4], b1[5], b1[6], b1[7]);
-  const unsigned d0 = o[0] ^ pack_low_bytes(b2[0], b2[1], b2[2], b2[3]);
-  const unsigned d1 = o[1] ^ pack_low_bytes(b2[4], b2[5], b2[6], b2[7]);
-  if (__builtin_expect((d0 | d1) != 0u, 0)) {
-    int c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = quant_code(static_cast<float>(x[e]), a);
-    o[0] = pack4(c[0], c[1], c[2], c[3]);
-    o[1] = pack4(c[4], c[5], c[6], c[7]);
-  }
-  return o;
-}
-
-// Exact codes of 8 halves under absmax a, for groups where the quant8_bracket pair
+// Exact codes of 8 halves under absmax a, for groups where the quant8_fast pair
 // disagreed. With w = |x| and q1 = RNE(w * lo) (lo = quant_bracket(a).lo <= 127 / a),
 // the code of w is q1 or q1 + 1; it is q1 + 1 exactly when 127 w / a > q1 + 1/2, or
 // equals it with q1 odd (half-even). That comparison, 254 w against (2 q1 + 1) a, is
@@ -166,8 +113,12 @@ __device__ __forceinline__ void drop_halves(v8h& v, unsigned drop) {
   v = __builtin_bit_cast(v8h, u);
 }
 
-// Codes of 8 halves from the bracketing pair (quant8_bracket without its fallback):
-// returns the lower bracket's codes and sets dis != 0 where the pair disagrees.
+// Codes of 8 halves under absmax a from the bracketing pair br = quant_bracket(a).
+// p_lo = x br.lo and p_hi = x br.hi bracket the exact 127 x / a, and round-half-even
+// is monotonic, so where both round to the same integer that integer is the exact
+// code. Returns the lower bracket's codes and sets dis != 0 where the pair disagrees
+// (a value within about 2^-15 of a half-integer, or an exact tie); those groups take
+// quant8_exact.
 __device__ __forceinline__ v2u quant8_fast(const v8h& x, QuantBracket br, unsigned& dis) {
   unsigned b1[8], b2[8];
 #pragma unroll
@@ -246,23 +197,6 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ unsigned wave_or(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
   return v;
 }
 

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const _Float16 px = a.X[static_cast<size_t>(min(pq, M - 1)) * K + pcol];
 
   // 7. codes into LDS, outlier columns cleared first (their codes are 0). The bracketing
-  // pair (see quant8_bracket) decides; (row, chunk) slots where it disagrees (values at
+  // pair (see quant8_fast) decides; (row, chunk) slots where it disagrees (values at
   // or within about 2^-15 of a half-integer) are rewritten with quant8_exact below.
   unsigned redo = 0;
 #pragma unroll

@@ -64,7 +64,7 @@ def fma32(a, b, c):
 
 
 def bracket_model(v16, a16):
-    """Emulates quant8_bracket and quant8_exact of the decode kernel: returns the
+    """Emulates quant8_fast and quant8_exact of the kernels: returns the
     lower-bracket codes, a flag per element where the pair disagrees, and the
     exact-path codes for every element."""
     a32 = np.float32(a16)
