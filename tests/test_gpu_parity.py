@@ -164,6 +164,23 @@ def test_mixed_matmul_parity(M, K, N):
     check_y(Y, ref["Y"])
 
 
+# one shape per decode instantiation (rows held 2/4/8/16 x k-steps per wave 2/4/8/16)
+DECODE_SHAPES = [(2, 528), (1, 2000), (2, 4000), (1, 8000), (3, 1008), (4, 1552), (3, 4080),
+                 (4, 8192), (6, 992), (7, 2032), (5, 4096), (6, 5456), (12, 720), (11, 1792),
+                 (10, 3264)]
+
+
+@pytest.mark.parametrize("M,K", DECODE_SHAPES)
+def test_decode_every_instantiation(M, K):
+    assert binding.is_decode(M, K)
+    announce(f"decode instantiation M={M} K={K}")
+    X = planted(5 * M + K, M, K, n_dims=4)
+    W = weight(K + 1, K, 80)
+    ref, Y, acc = _mixed(X, W, 6.0, mo=min(256, K))
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
 @pytest.mark.parametrize("M,K,N", [(16, 1024, 256), (200, 1040, 528)])
 def test_zero_outlier_invariant(M, K, N):
     """t = +inf: no outlier columns; Y is the dequantized int8 product."""
