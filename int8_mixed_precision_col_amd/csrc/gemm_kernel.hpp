@@ -24,9 +24,9 @@
 // belongs at its LDS slot under an XOR swizzle, so that the ds_read_b128 fragment
 // reads are free of bank conflicts. Slab kt + STAGES - 1 is in
 // flight while slab kt is multiplied; one barrier per slab.
-// The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, reading the
-// small Xo / WoT fragments straight from global memory (L2-resident), accumulating
-// on top of the already dequantized fp32 values before the single rounding to fp16.
+// The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, with the
+// small Xo / WoT fragments staged through LDS, accumulating on top of the already
+// dequantized fp32 values before the single rounding to fp16.
 #pragma once
 
 #include "common.hpp"
@@ -119,51 +119,114 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The LDS ring: one __shared__ object per stage, so that the compiler can tell which
+// stage a DMA writes and a fragment read reads (a single array indexed by stage makes
+// it wait for every outstanding DMA before each read).
+template <class C, int S>
+__device__ __forceinline__ char* stage_buf() {
+  __shared__ __attribute__((aligned(1024))) char buf[C::STAGE];
+  return buf;
+}
+
+// Epilogue. 32x32 accumulator layout: lane l, register r holds column m = l % 32 and
+// row n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). The tile's
+// a_w / a_x and the outlier fragments (16 columns of WoT and Xo per pass) are staged
+// in stage 0 of the ring first (free once the K loop is done), so that no global
+// load waits inside the per-block loops; reading them straight from global memory,
+// one block of 32 x 32 at a time, took ~13 us per tile against ~8 us now. Per block:
+// store the int32 sums if asked, dequantize in place to fp32, let the fp16 outlier
+// MFMA accumulate on top of that, round once to fp16.
 template <class C>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::BN][C::BM],
-                                              int n0, int m0, int wn, int wm, int lane) {
-  // 32x32 accumulator layout: lane l, register r holds column m = l % 32 and row
-  // n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). Per block:
-  // store the int32 sums if asked, dequantize in place to fp32, let the fp16 outlier
-  // MFMA accumulate on top of that, round once to fp16.
+                                                     int n0, int m0, int wn, int wm, int lane,
+                                                     int tid) {
+  constexpr int OS = 24;  // staged row stride in halves (16 columns + 8 of padding)
+  static_assert((C::TN + C::TM) * 4 + (C::TN + C::TM) * OS * 2 <= C::STAGE, "staging fits a stage");
+  char* base = stage_buf<C, 0>();
+  float* aw_s = reinterpret_cast<float*>(base);
+  float* ax_s = aw_s + C::TN;
+  _Float16* wo_s = reinterpret_cast<_Float16*>(ax_s + C::TM);
+  _Float16* xo_s = wo_s + C::TN * OS;
   const int l32 = lane & 31, lhi = lane >> 5;
   const int count = *g.count;
   const bool overflow = count > g.max_outliers;
   const int o_pad = min((count + 15) & ~15, g.o_stride);
   const int M = g.M, N = g.N;
+  auto stage_outliers = [&](int s0) {
+    for (int t = tid; t < (C::TN + C::TM) * 2; t += C::NT) {
+      const int row = t >> 1, h = t & 1;
+      if (row < C::TN)
+        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) = *reinterpret_cast<const v8h*>(
+            g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h);
+      else
+        *reinterpret_cast<v8h*>(xo_s + (row - C::TN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
+            g.Xo + static_cast<size_t>(min(m0 + row - C::TN, M - 1)) * g.o_stride + s0 + 8 * h);
+    }
+  };
+  lds_reads_done();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
+  asm volatile("" ::: "memory");
+  for (int t = tid; t < C::TN + C::TM; t += C::NT) {
+    if (t < C::TN) aw_s[t] = g.a_w[min(n0 + t, N - 1)];
+    else ax_s[t - C::TN] = g.a_x[min(m0 + t - C::TN, M - 1)];
+  }
+  if (o_pad > 0) stage_outliers(0);
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < C::BN; ++i) {
-    const int nb = n0 + wn * C::WTN + i * 32;
-    const _Float16* wo_row = g.WoT + static_cast<size_t>(min(nb + l32, N - 1)) * g.o_stride;
+    const int nl = wn * C::WTN + i * 32;
 #pragma unroll
     for (int j = 0; j < C::BM; ++j) {
-      const int m = m0 + wm * C::WTM + j * 32 + l32;
-      const int mc = min(m, M - 1);
-      const float sx = g.a_x[mc] * kInvQMax2;
+      const int ml = wm * C::WTM + j * 32;
+      const int m = m0 + ml + l32;
+      const float sx = ax_s[ml + l32] * kInvQMax2;
       v16f y;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nb + 8 * q + 4 * lhi;
-        const v4f aw = n < N ? *reinterpret_cast<const v4f*>(g.a_w + n) : v4f{};
-        if (g.acc_out && m < M && n < N) {
+        const int nq = nl + 8 * q + 4 * lhi;
+        const v4f aw = *reinterpret_cast<const v4f*>(aw_s + nq);
+        if (g.acc_out && m < M && n0 + nq < N) {
           const v4i av = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]};
-          *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(m) * N + n) = av;
+          *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(m) * N + n0 + nq) = av;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[4 * q + e] = static_cast<float>(acc[i][j][4 * q + e]) * sx * aw[e];
+        for (int e = 0; e < 4; ++e) y[4 * q + e] = static_cast<float>(acc[i][j][4 * q + e]) * sx * aw[e];
       }
-      const _Float16* xo_row = g.Xo + static_cast<size_t>(mc) * g.o_stride;
-      for (int s = 0; s < o_pad; s += 16) {
-        const v8h fa = *reinterpret_cast<const v8h*>(wo_row + s + 8 * lhi);
-        const v8h fb = *reinterpret_cast<const v8h*>(xo_row + s + 8 * lhi);
-        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
+      acc[i][j] = __builtin_bit_cast(v16i, y);
+    }
+  }
+  for (int s0 = 0; s0 < o_pad; s0 += 16) {
+    if (s0 > 0) {
+      lds_barrier();
+      stage_outliers(s0);
+      lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < C::BN; ++i) {
+      const int nl = wn * C::WTN + i * 32;
+#pragma unroll
+      for (int j = 0; j < C::BM; ++j) {
+        const int ml = wm * C::WTM + j * 32;
+        const v8h fa = *reinterpret_cast<const v8h*>(wo_s + (nl + l32) * OS + 8 * lhi);
+        const v8h fb = *reinterpret_cast<const v8h*>(xo_s + (ml + l32) * OS + 8 * lhi);
+        acc[i][j] = __builtin_bit_cast(v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                                 fa, fb, __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
       }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::BN; ++i) {
+    const int nl = wn * C::WTN + i * 32;
+#pragma unroll
+    for (int j = 0; j < C::BM; ++j) {
+      const int m = m0 + wm * C::WTM + j * 32 + l32;
       if (m < M) {
+        const v16f y = __builtin_bit_cast(v16f, acc[i][j]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = nb + 8 * q + 4 * lhi;
+          const int n = n0 + nl + 8 * q + 4 * lhi;
           if (n < N) {
             v4h out;
 #pragma unroll
@@ -176,15 +239,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
       }
     }
   }
-}
-
-// The LDS ring: one __shared__ object per stage, so that the compiler can tell which
-// stage a DMA writes and a fragment read reads (a single array indexed by stage makes
-// it wait for every outstanding DMA before each read).
-template <class C, int S>
-__device__ __forceinline__ char* stage_buf() {
-  __shared__ __attribute__((aligned(1024))) char buf[C::STAGE];
-  return buf;
 }
 
 template <class C>
@@ -382,7 +436,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
   }
   // no DMA may still be writing this block's LDS when the block exits
   __builtin_amdgcn_s_waitcnt(0);
-  gemm_epilogue<C>(g, b.acc, n0, m0, b.wn, b.wm, b.lane);
+  gemm_epilogue<C>(g, b.acc, n0, m0, b.wn, b.wm, b.lane, tid);
 }
 
 #undef I8MM_LDS
