@@ -229,6 +229,51 @@ def cpu_baseline(oracle, X, W, wl, budget_s: float = 15.0) -> dict:
                       f"(numpy float64 BLAS on {cores} threads)"}
 
 
+def bench_projections(binding, torch, inputs, reps: int = 10) -> dict:
+    """Three projections of one input (Q, K, V: 2048 x 4096 times three 4096 x 4096
+    weights, drawn like opt6.7b_ffn_up): three int8_mixed_matmul calls, one
+    activation quantization + three int8_mixed_matmul_q calls, and one quantization +
+    one grouped launch. Each alone is 128 tiles of 256 x 256 for 256 CUs."""
+    wl = inputs.WORKLOADS["opt6.7b_ffn_up"]
+    X, _ = inputs.make_x(wl)
+    W = inputs.make_w(wl)
+    Xd = torch.from_numpy(X).cuda()
+    weights = [binding.prepare_weight(torch.from_numpy(np.ascontiguousarray(W[:, q * 4096:(q + 1) * 4096])).cuda())
+               for q in range(3)]
+    ws = binding.make_workspace(wl.M, wl.K, 4096, MAX_OUTLIERS)
+    outs = [torch.empty((wl.M, 4096), dtype=torch.float16, device="cuda") for _ in range(3)]
+    ops = 3 * 2.0 * wl.M * wl.K * 4096
+
+    def separate():
+        for (Wq, aw), Y in zip(weights, outs):
+            binding.mixed_matmul(Xd, Wq, aw, wl.threshold, MAX_OUTLIERS, workspace=ws, out=Y)
+
+    def quantize_once():
+        st = binding.QuantizedActivations(Xd, wl.threshold, MAX_OUTLIERS)
+        for (Wq, aw), Y in zip(weights, outs):
+            st.matmul(Wq, aw, out=Y)
+
+    def grouped():
+        st = binding.QuantizedActivations(Xd, wl.threshold, MAX_OUTLIERS)
+        st.matmul_grouped(weights, outs=outs)
+
+    res = {"workload": "opt6.7b qkv: M=2048 K=4096 N=3x4096", "unit": "TOPS"}
+    for name, fn in (("three_calls", separate), ("quantize_once", quantize_once),
+                     ("grouped_launch", grouped)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": ms, "TOPS": ops / (ms * 1e-3) / 1e12}
+    return res
+
+
 def bench_decode(binding, torch, inputs, reps: int) -> dict:
     """Decode shape: 32 calls over 32 distinct prepared weights (2x the MALL) captured
     in one HIP graph, as a decode step walks the layers; per-call time = replay time /
@@ -391,6 +436,9 @@ def main() -> int:
     if args.traffic_probe:
         log("traffic probe done")
         return 0
+    if not args.no_decode:
+        log("projections sharing one input")
+        result["projections_qkv"] = bench_projections(binding, torch, inputs)
     if not args.no_cpu_baseline:
         import oracle
 

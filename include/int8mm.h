@@ -161,6 +161,28 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
                         hipStream_t stream);
 
 /*
+ * int8_mixed_matmul_q for G <= 8 weights at once, in one GEMM launch: the weights'
+ * output tiles form one grid, so projections too narrow to fill the GPU on their
+ * own (Q, K, V of one layer) run side by side ([Abstract]: the attention and
+ * feed-forward projection layers share the input the state was made from).
+ *   G             1 <= G <= 8.
+ *   Wq, w_absmax, N, Y   host arrays of G entries (read during the call, not kept):
+ *                 each weight's unit-tiled int8 matrix, fp32 [N[q]] constants, output
+ *                 width (multiple of 16) and fp16 output [M, N[q]].
+ *   workspace     at least int8_mixed_matmul_q_grouped_workspace_bytes(G, N,
+ *                 max_outliers) bytes (the weights' outlier rows, one after another).
+ * Each Y[q] equals int8_mixed_matmul_q's output for that weight bit for bit. No
+ * int32 sums output. Errors as for int8_mixed_matmul_q; G out of range or a bad
+ * N[q] is INT8MM_E_SHAPE, a null entry INT8MM_E_NULL.
+ */
+size_t int8_mixed_matmul_q_grouped_workspace_bytes(int64_t G, const int64_t* N,
+                                                    int64_t max_outliers);
+int int8_mixed_matmul_q_grouped(const void* state, int64_t M, int64_t K, int64_t max_outliers,
+                                int64_t G, const int8_t* const* Wq, const float* const* w_absmax,
+                                const int64_t* N, void* const* Y, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Weight-only int8 product for a handful of tokens: Y = X · Ŵ with
  * Ŵ[k, n] = Wq[n, k] · w_absmax[n] / 127, no activation quantization and no
  * outlier decomposition ("What is 8-bit LLM quantization?", What is special about

@@ -35,6 +35,9 @@ SIGNATURES = {
     "int8_mixed_matmul_q_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_mixed_matmul_q": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, ctypes.c_size_t,
                                    _p, _p]),
+    "int8_mixed_matmul_q_grouped_workspace_bytes": (ctypes.c_size_t, [_i64, _p, _i64]),
+    "int8_mixed_matmul_q_grouped": (_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
+                                           ctypes.c_size_t, _p]),
     "int8mm_read_status": (_int, [_p, _p, _p]),
     "int8mm_strerror": (ctypes.c_char_p, [_int]),
     "int8mm_timing_enable": (_int, [_int]),
@@ -241,6 +244,38 @@ class QuantizedActivations:
                                          acc_out.data_ptr() if acc_out is not None else None,
                                          _stream(Wq)), "int8_mixed_matmul_q")
         return out
+
+    def matmul_grouped(self, weights: list, outs: list | None = None,
+                       workspace: torch.Tensor | None = None) -> list:
+        """Y fp16 [M, N_q] for each (Wq, a_w) in `weights` (at most 8), from this
+        quantized X, in one GEMM launch."""
+        G = len(weights)
+        Ns = []
+        for Wq, a_w in weights:
+            _need(Wq, torch.int8, "Wq")
+            _need(a_w, torch.float32, "a_w")
+            if Wq.numel() != int(lib().int8_prepared_weight_bytes(self.K, a_w.shape[0])):
+                raise ValueError("Wq does not match (K, N)")
+            Ns.append(a_w.shape[0])
+        dev = weights[0][0].device
+        if outs is None:
+            outs = [torch.empty((self.M, n), dtype=torch.float16, device=dev) for n in Ns]
+        for o in outs:
+            _need(o, torch.float16, "out")
+        n_arr = (_i64 * G)(*Ns)
+        wb = int(lib().int8_mixed_matmul_q_grouped_workspace_bytes(G, n_arr, self.max_outliers))
+        if workspace is None:
+            workspace = torch.empty((max(wb, 1),), dtype=torch.uint8, device=dev)
+        _need(workspace, torch.uint8, "workspace")
+        wq_arr = (_p * G)(*[w.data_ptr() for w, _ in weights])
+        aw_arr = (_p * G)(*[a.data_ptr() for _, a in weights])
+        y_arr = (_p * G)(*[o.data_ptr() for o in outs])
+        _check(lib().int8_mixed_matmul_q_grouped(self.state.data_ptr(), self.M, self.K,
+                                                 self.max_outliers, G, wq_arr, aw_arr, n_arr,
+                                                 y_arr, workspace.data_ptr(), workspace.numel(),
+                                                 _stream(workspace)),
+               "int8_mixed_matmul_q_grouped")
+        return outs
 
 
 def read_status(workspace: torch.Tensor) -> tuple[int, int]:

@@ -17,6 +17,28 @@ static hipError_t run(const GemmArgs& g, hipStream_t s, int group_m) {
   return hipGetLastError();
 }
 
+template <class C>
+static hipError_t run_grouped(GroupedGemmArgs& a, hipStream_t s, int group_m) {
+  const int tiles_m = (a.base.M + C::TM - 1) / C::TM;
+  int tn = 0;
+  for (int q = 0; q < a.G; ++q) {
+    a.tn_first[q] = tn;
+    tn += (a.N[q] + C::TN - 1) / C::TN;
+  }
+  for (int q = a.G; q <= kMaxGroups; ++q) a.tn_first[q] = tn;
+  if (group_m > tiles_m) group_m = tiles_m;
+  hipLaunchKernelGGL(k_gemm_grouped<C>, dim3(tn * tiles_m), dim3(C::NT), 0, s, a, tiles_m, group_m);
+  return hipGetLastError();
+}
+
+// Same choice of tile shape as launch_gemm, on the combined tile count.
+hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
+  long tiles_l = 0;
+  for (int q = 0; q < a.G; ++q) tiles_l += static_cast<long>((a.N[q] + 255) / 256) * ((a.base.M + 255) / 256);
+  if (a.base.M >= 256 && tiles_l >= 256) return run_grouped<CfgL>(a, s, 8);
+  return run_grouped<CfgS>(a, s, 8);
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const long tiles_l = static_cast<long>((g.N + 255) / 256) * ((g.M + 255) / 256);
   if (g.M >= 256 && tiles_l >= 256) return run<CfgL>(g, s, 8);

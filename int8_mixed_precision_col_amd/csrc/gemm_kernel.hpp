@@ -371,8 +371,10 @@ struct GemmBlock {
   }
 };
 
+// One output tile (tn, tm) of the product described by g: the whole K loop and the
+// epilogue.
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int group_m) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
   GemmBlock<C> b{g};
   const int tid = threadIdx.x;
   b.lane = tid & 63;
@@ -387,8 +389,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
     b.rn0 = (vw % C::WGN) * C::WTN + (b.lane & 31);
     b.rm0 = (vw / C::WGN) * C::WTM + (b.lane & 31);
   }
-  int tn, tm;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, group_m, tn, tm);
   const int n0 = tn * C::TN, m0 = tm * C::TM;
   const int K = g.K;
   // LDS slot p = 64 (i NW + wave) + lane of a tile holds row p / CPR, chunk
@@ -437,6 +437,34 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
   // no DMA may still be writing this block's LDS when the block exits
   __builtin_amdgcn_s_waitcnt(0);
   gemm_epilogue<C>(g, b.acc, n0, m0, b.wn, b.wm, b.lane, tid);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int group_m) {
+  int tn, tm;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, group_m, tn, tm);
+  gemm_tile<C>(g, tn, tm);
+}
+
+// Several weights against one quantized activation in one launch: the groups' column
+// tiles are laid side by side (group q owns virtual tile columns [tn_first[q],
+// tn_first[q + 1])), the XCD-aware order runs over that combined grid, and each block
+// multiplies with its group's weight, constants, outlier rows and output.
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_gemm_grouped(GroupedGemmArgs ga, int tiles_m,
+                                                        int group_m) {
+  int tnv, tm;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, group_m, tnv, tm);
+  int q = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) q += (i < ga.G && tnv >= ga.tn_first[i]) ? 1 : 0;
+  GemmArgs g = ga.base;
+  g.Wq = ga.Wq[q];
+  g.a_w = ga.a_w[q];
+  g.WoT = ga.WoT[q];
+  g.Y = ga.Y[q];
+  g.N = ga.N[q];
+  gemm_tile<C>(g, tnv - ga.tn_first[q], tm);
 }
 
 #undef I8MM_LDS

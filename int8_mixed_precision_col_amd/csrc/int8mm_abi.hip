@@ -279,6 +279,67 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
   return timing_end(stream);
 }
 
+size_t int8_mixed_matmul_q_grouped_workspace_bytes(int64_t G, const int64_t* N,
+                                                    int64_t max_outliers) {
+  if (G < 1 || G > i8mm::kMaxGroups || !N) return 0;
+  size_t total = 0;
+  for (int64_t q = 0; q < G; ++q) {
+    const size_t b = int8_mixed_matmul_q_workspace_bytes(N[q], max_outliers);
+    if (b == 0) return 0;
+    total += b;
+  }
+  return total;
+}
+
+int int8_mixed_matmul_q_grouped(const void* state, int64_t M, int64_t K, int64_t max_outliers,
+                                int64_t G, const int8_t* const* Wq, const float* const* w_absmax,
+                                const int64_t* N, void* const* Y, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!state || !Wq || !w_absmax || !N || !Y || !workspace) return INT8MM_E_NULL;
+  if (G < 1 || G > i8mm::kMaxGroups) return INT8MM_E_SHAPE;
+  for (int64_t q = 0; q < G; ++q)
+    if (!Wq[q] || !w_absmax[q] || !Y[q]) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  for (int64_t q = 0; q < G; ++q)
+    if (bad_n(N[q])) return INT8MM_E_SHAPE;
+  if (!aligned16(state) || !aligned16(workspace)) return INT8MM_E_ALIGN;
+  for (int64_t q = 0; q < G; ++q)
+    if (!aligned16(Wq[q]) || !aligned16(w_absmax[q]) || !aligned16(Y[q])) return INT8MM_E_ALIGN;
+  if (workspace_bytes < int8_mixed_matmul_q_grouped_workspace_bytes(G, N, max_outliers))
+    return INT8MM_E_WORKSPACE;
+  const Layout L = prefill_layout(M, K, 0, max_outliers);
+  const char* st = static_cast<const char*>(state);
+  const int32_t* status = reinterpret_cast<const int32_t*>(st + L.status);
+  i8mm::GroupedGemmArgs ga{};
+  i8mm::GemmArgs& g = ga.base;
+  g.Xq = reinterpret_cast<const int8_t*>(st + L.xq); g.M = int(M); g.K = int(K);
+  g.a_x = reinterpret_cast<const float*>(st + L.a_x);
+  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo); g.o_stride = L.o_stride;
+  g.count = status + 1; g.max_outliers = int(max_outliers); g.acc_out = nullptr;
+  ga.G = int(G);
+  char* ws = static_cast<char*>(workspace);
+  for (int64_t q = 0; q < G; ++q) {
+    // each weight's dequantized outlier rows, gathered from the shared outlier list
+    _Float16* wot = reinterpret_cast<_Float16*>(ws);
+    ws += int8_mixed_matmul_q_workspace_bytes(N[q], max_outliers);
+    i8mm::QuantRowsArgs qa{};
+    qa.M = int(M); qa.K = int(K);
+    qa.partial = reinterpret_cast<const uint32_t*>(st + L.partial); qa.R = L.R;
+    qa.gather_only = 1;
+    qa.count_out = nullptr; qa.status_out = nullptr; qa.idx_out = nullptr;
+    qa.max_outliers = int(max_outliers);
+    qa.o_stride = L.o_stride;
+    qa.Wq = Wq[q]; qa.a_w = w_absmax[q]; qa.N = int(N[q]); qa.WoT = wot;
+    if (i8mm::launch_quant_rows(qa, stream) != hipSuccess) return INT8MM_E_HIP;
+    ga.Wq[q] = Wq[q]; ga.a_w[q] = w_absmax[q]; ga.WoT[q] = wot;
+    ga.Y[q] = static_cast<_Float16*>(Y[q]); ga.N[q] = int(N[q]);
+  }
+  int rc;
+  if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
+  if (i8mm::launch_gemm_grouped(ga, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream);
+}
+
 int int8_weight_only_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                             const float* w_absmax, int64_t N, void* Y, hipStream_t stream) {
   if (!X || !Wq || !w_absmax || !Y) return INT8MM_E_NULL;

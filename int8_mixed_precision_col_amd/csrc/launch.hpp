@@ -53,6 +53,21 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// Up to kMaxGroups weights sharing one activation state (base holds the shared fields;
+// its Wq, a_w, WoT, Y, N are unused).
+constexpr int kMaxGroups = 8;
+struct GroupedGemmArgs {
+  GemmArgs base;
+  int G;
+  const int8_t* Wq[kMaxGroups];
+  const float* a_w[kMaxGroups];
+  const _Float16* WoT[kMaxGroups];
+  _Float16* Y[kMaxGroups];
+  int N[kMaxGroups];
+  int tn_first[kMaxGroups + 1];  // first virtual tile column of each group (filled by the launcher)
+};
+hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s);
+
 struct DecodeArgs {
   const _Float16* X;  // [M][K]
   int M, K;

@@ -141,3 +141,26 @@ def test_quantize_once_rejects_and_sizes(L):
     assert mq(P, 64, 256, 16, P, P, 120, P, P, wb, None, None) == E_SHAPE
     assert mq(P, 64, 256, 16, P, P, 128, UNALIGNED, P, wb, None, None) == E_ALIGN
     assert mq(P, 64, 256, 16, P, P, 128, P, P, wb - 1, None, None) == E_WS
+
+
+def test_grouped_rejects_and_sizes(L):
+    I64 = ctypes.c_int64
+    P_ = ctypes.c_void_p
+    ns = (I64 * 3)(512, 272, 1040)
+    wb = L.int8_mixed_matmul_q_grouped_workspace_bytes(3, ns, 16)
+    assert wb == sum(L.int8_mixed_matmul_q_workspace_bytes(n, 16) for n in (512, 272, 1040))
+    assert L.int8_mixed_matmul_q_grouped_workspace_bytes(0, ns, 16) == 0
+    assert L.int8_mixed_matmul_q_grouped_workspace_bytes(9, (I64 * 9)(*[64] * 9), 16) == 0
+    assert L.int8_mixed_matmul_q_grouped_workspace_bytes(1, (I64 * 1)(24), 16) == 0
+    ptrs = (P_ * 3)(P, P, P)
+    g = L.int8_mixed_matmul_q_grouped
+    assert g(None, 64, 256, 16, 3, ptrs, ptrs, ns, ptrs, P, wb, None) == E_NULL
+    assert g(P, 64, 256, 16, 3, None, ptrs, ns, ptrs, P, wb, None) == E_NULL
+    assert g(P, 64, 256, 16, 3, (P_ * 3)(P, None, P), ptrs, ns, ptrs, P, wb, None) == E_NULL
+    assert g(P, 64, 256, 16, 0, ptrs, ptrs, ns, ptrs, P, wb, None) == E_SHAPE
+    assert g(P, 64, 256, 16, 9, (P_ * 9)(*[P] * 9), (P_ * 9)(*[P] * 9), (I64 * 9)(*[64] * 9),
+             (P_ * 9)(*[P] * 9), P, 1 << 30, None) == E_SHAPE
+    assert g(P, 64, 256, 16, 3, ptrs, ptrs, (I64 * 3)(512, 24, 1040), ptrs, P, wb, None) == E_SHAPE
+    assert g(P, 64, 250, 16, 3, ptrs, ptrs, ns, ptrs, P, wb, None) == E_SHAPE
+    assert g(P, 64, 256, 16, 3, ptrs, (P_ * 3)(P, UNALIGNED, P), ns, ptrs, P, wb, None) == E_ALIGN
+    assert g(P, 64, 256, 16, 3, ptrs, ptrs, ns, ptrs, P, wb - 1, None) == E_WS

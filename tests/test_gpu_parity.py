@@ -330,3 +330,22 @@ def test_quantize_once_feeds_several_weights(M, K, Ns):
         if not binding.is_decode(M, K):
             Y1 = binding.mixed_matmul(Xd, Wq, aw, 6.0, 256)
             assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
+                                    (2048, 1024, (4096, 4096, 4096)),
+                                    (257, 528, (16, 48, 80, 272, 528, 16, 32, 64))])
+def test_grouped_launch_equals_per_weight_calls(M, K, Ns):
+    """One grouped GEMM launch over several weights: every output equals the
+    one-weight int8_mixed_matmul_q call bit for bit (small- and large-tile grids)."""
+    announce(f"grouped launch M={M} K={K} Ns={Ns}")
+    X = planted(M + K + len(Ns), M, K, n_dims=3)
+    state = binding.QuantizedActivations(dev(X), 6.0, 64)
+    weights = [binding.prepare_weight(dev(weight(M + q, K, n))) for q, n in enumerate(Ns)]
+    got = state.matmul_grouped(weights)
+    for (Wq, aw), Yg in zip(weights, got):
+        Y1 = state.matmul(Wq, aw)
+        assert np.array_equal(host(Yg).view(np.uint16), host(Y1).view(np.uint16))
+    # and against the oracle for the first weight
+    Wq_ref, aw_ref = oracle.prepare_weight(weight(M, K, Ns[0]))
+    check_y(host(got[0]), oracle.mixed_matmul(X, Wq_ref, aw_ref, 6.0)["Y"])
