@@ -373,8 +373,9 @@ def main() -> int:
         summarize_traffic(*args.summarize_traffic, args.workload, args.command)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
+              "library runs on one GPU (several GPUs would split the weight's output "
+              "columns, with no exchange needed before the matmul)", file=sys.stderr)
         return 2
 
     import torch
