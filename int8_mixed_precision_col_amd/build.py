@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -26,7 +27,24 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def _check_no_scratch(src: str, diagnostics: str) -> None:
+    """Every kernel keeps its private data in registers: a kernel with per-lane
+    scratch memory (a dynamically indexed array or a register spill) fails the build,
+    since it would run many times slower than designed."""
+    name = None
+    for line in diagnostics.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: kernel {name} uses {m.group(1)} bytes/lane of scratch")
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -37,6 +55,7 @@ def _compile(src: str, verbose: bool) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    _check_no_scratch(src, r.stderr)
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
     return obj

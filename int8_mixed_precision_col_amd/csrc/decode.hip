@@ -28,7 +28,9 @@
 
 namespace i8mm {
 
-constexpr int kDecMaxM = 16, kDecMaxK = 8192, kDecMaxMK = 32768;
+constexpr int kDecMaxM = 16, kDecMaxK = 8192;
+// dynamic LDS a block may take (160 KB per CU, less the kernel's static arrays)
+constexpr size_t kDecMaxDynLds = 150 * 1024;
 constexpr int kDecWaves = 8, kDecThreads = 64 * kDecWaves;
 constexpr int kOutChunk = 64;  // outlier columns staged in LDS per epilogue pass
 constexpr int kPre = kDecThreads / 16;  // outlier columns gathered before the MFMA (32)
@@ -45,9 +47,20 @@ static int steps_per_wave(int64_t K) {
   return max(2, pow2_at_least(static_cast<int>((K + 511) / 512)));
 }
 
-// M K <= 32768 keeps Xq and the registers of X within budget (K > 4096 allows M <= 7).
+// X chunks a thread holds in registers: rows_held(M) x (one per 4096 columns of K),
+// at most 16 (64 registers): M <= 16 up to K = 4096, M <= 8 up to K = 8192.
 bool decode_supported(int64_t M, int64_t K) {
-  return M >= 1 && M <= kDecMaxM && K <= kDecMaxK && M * K <= kDecMaxMK;
+  if (M < 1 || M > kDecMaxM || K > kDecMaxK) return false;
+  return rows_held(M) * (K > 4096 ? 2 : 1) <= 16;
+}
+
+// Dynamic LDS of one block; with x_staged, the masked copy of X is included.
+static size_t decode_lds_bytes(int64_t M, int64_t K, bool x_staged) {
+  const size_t nchunk = static_cast<size_t>(K) / 8;
+  const size_t off_flag = (x_staged ? static_cast<size_t>(M) * K * 2 : 0) +
+                          ((static_cast<size_t>(M) * (K + 16) + 15) & ~size_t(15));
+  const size_t head = off_flag + ((nchunk + 3) & ~size_t(3)) + static_cast<size_t>(K) * 2;
+  return ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 16;
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
@@ -92,10 +105,11 @@ __device__ __forceinline__ void wave_max_u32_n(unsigned (&v)[N]) {
 }
 
 // MR: token rows held per thread (M <= MR), SPW: MFMA k-steps per wave (slots for the
-// weight units). Thread t owns the 8-column chunks c = 64 ((w + xrot) mod 8) + l + 512 j
+// weight units), XS: the masked X is staged in LDS for the exact pass (else that pass
+// reads X from global memory, where the larger shapes leave no room in LDS). Thread t owns the 8-column chunks c = 64 ((w + xrot) mod 8) + l + 512 j
 // (w its wave, l its lane, j < CC) of every row, so a chunk's outlier test over all
 // rows and its keep-mask are computed once, in registers.
-template <int MR, int SPW>
+template <int MR, int SPW, bool XS>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   constexpr int CC = SPW > 8 ? 2 : 1;  // chunks per thread: K <= 4096 needs one
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -106,10 +120,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int K = a.K, M = a.M;
   const int W = (K + 31) / 32, nchunk = K / 8, xs = K + 16;
   const int nflag = (nchunk + 3) & ~3;
-  // LDS: X with its outlier columns cleared [M][K] | Xq [M][K + 16] | outlier bits, one
-  // byte per chunk [nflag] | outlier column list [K] (short) | outlier staging | sink
+  // LDS: X with its outlier columns cleared [M][K] (XS only) | Xq [M][K + 16] |
+  // outlier bits, one byte per chunk [nflag] | outlier column list [K] (short) |
+  // outlier staging | sink
   _Float16* x_s = reinterpret_cast<_Float16*>(lds);
-  const int off_xq = M * K * 2;
+  const int off_xq = XS ? M * K * 2 : 0;
   int8_t* xq_s = reinterpret_cast<int8_t*>(lds + off_xq);
   const int off_flag = off_xq + ((M * xs + 15) & ~15);
   unsigned char* flag_s = reinterpret_cast<unsigned char*>(lds + off_flag);
@@ -266,7 +281,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   unsigned redo = 0;
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    if (m >= M) break;  // block-uniform
+    // a skipped body rather than an early exit: the loop must unroll fully so that
+    // xv stays in registers (a loop with a second exit is left rolled at MR = 16,
+    // and xv[m] then lives in scratch memory)
+    if (m >= M) continue;  // block-uniform
     const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
     const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.hi), m));
 #pragma unroll
@@ -276,8 +294,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) u[d] &= keep[j][d];
       xv[m][j] = __builtin_bit_cast(v8h, u);
-      *reinterpret_cast<v8h*>(c < nchunk ? reinterpret_cast<char*>(x_s + m * K + c * 8)
-                                         : reinterpret_cast<char*>(sink_s + lane * 16)) = xv[m][j];
+      if constexpr (XS)
+        *reinterpret_cast<v8h*>(c < nchunk ? reinterpret_cast<char*>(x_s + m * K + c * 8)
+                                           : reinterpret_cast<char*>(sink_s + lane * 16)) = xv[m][j];
       unsigned b1[8], b2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -306,7 +325,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     const bool any = jb < static_cast<unsigned>(MR * CC);
     const int ms = any ? static_cast<int>(jb) / CC : 0;
     const int cs = cbase + 512 * (any ? static_cast<int>(jb) % CC : 0);
-    const v8h x = *reinterpret_cast<const v8h*>(x_s + (any ? ms * K + cs * 8 : 0));
+    // the pending chunk: the masked copy in LDS, or X itself, whose outlier columns
+    // are then left out below (their codes are 0 already)
+    const v8h x = XS ? *reinterpret_cast<const v8h*>(x_s + (any ? ms * K + cs * 8 : 0))
+                     : *reinterpret_cast<const v8h*>(a.X + (any ? static_cast<size_t>(ms) * K + cs * 8 : 0));
     const float am = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, am_l)));
     const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, br_l.lo)));
     const float hi = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(ms << 2, __builtin_bit_cast(int, br_l.hi)));
@@ -319,6 +341,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       diff |= t1 != t2 ? 1u << e : 0u;
     }
     diff &= ~done;
+    if constexpr (!XS) diff &= ~static_cast<unsigned>(flag_s[any ? cs : 0]);
     const int e = __builtin_ctz(diff | 0x100u);  // 8: nothing left in this slot
     const unsigned xd = __builtin_bit_cast(v4u, x)[(e >> 1) & 3];
     const float xf = half_bits_to_float((e & 1) ? xd >> 16 : xd & 0xffffu);
@@ -402,23 +425,22 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const int nchunk = a.K / 8;
-  const size_t off_flag = static_cast<size_t>(a.M) * a.K * 2 +
-                          ((static_cast<size_t>(a.M) * (a.K + 16) + 15) & ~size_t(15));
-  const size_t head = off_flag + static_cast<size_t>((nchunk + 3) & ~3) +
-                      static_cast<size_t>(a.K) * 2;
-  const size_t lds = ((head + 15) & ~size_t(15)) + 2 * kOutChunk * 16 * sizeof(float) + 64 * 16;
+  const bool xs = decode_lds_bytes(a.M, a.K, true) <= kDecMaxDynLds;
+  const size_t lds = decode_lds_bytes(a.M, a.K, xs);
   const int mr = rows_held(a.M), spw = steps_per_wave(a.K);
   const dim3 grid(a.N / 16), block(kDecThreads);
-#define I8MM_DEC(R, P)                                                              \
-  if (mr == R && spw == P) {                                                        \
-    hipLaunchKernelGGL((k_decode<R, P>), grid, block, lds, s, a);                   \
+#define I8MM_DEC(R, P, X)                                                           \
+  if (mr == R && spw == P && xs == X) {                                             \
+    hipLaunchKernelGGL((k_decode<R, P, X>), grid, block, lds, s, a);                \
     return hipGetLastError();                                                       \
   }
-  I8MM_DEC(2, 2) I8MM_DEC(2, 4) I8MM_DEC(2, 8) I8MM_DEC(2, 16)
-  I8MM_DEC(4, 2) I8MM_DEC(4, 4) I8MM_DEC(4, 8) I8MM_DEC(4, 16)
-  I8MM_DEC(8, 2) I8MM_DEC(8, 4) I8MM_DEC(8, 8) I8MM_DEC(8, 16)
-  I8MM_DEC(16, 2) I8MM_DEC(16, 4) I8MM_DEC(16, 8)
+  I8MM_DEC(2, 2, true) I8MM_DEC(2, 4, true) I8MM_DEC(2, 8, true) I8MM_DEC(2, 16, true)
+  I8MM_DEC(4, 2, true) I8MM_DEC(4, 4, true) I8MM_DEC(4, 8, true) I8MM_DEC(4, 16, true)
+  I8MM_DEC(8, 2, true) I8MM_DEC(8, 4, true) I8MM_DEC(8, 8, true) I8MM_DEC(8, 16, true)
+  I8MM_DEC(16, 2, true) I8MM_DEC(16, 4, true) I8MM_DEC(16, 8, true)
+  // shapes whose masked X does not fit beside Xq (M = 16 from K = 2880, M = 8 from
+  // K = 5536)
+  I8MM_DEC(8, 16, false) I8MM_DEC(16, 8, false)
 #undef I8MM_DEC
   return hipErrorInvalidValue;
 }

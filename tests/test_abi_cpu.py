@@ -96,7 +96,12 @@ def test_workspace_sizes(L):
     assert L.int8_mixed_matmul_is_decode(8, 4096) == 1 and ws(8, 4096, 4096, 256) == 256
     assert L.int8_mixed_matmul_is_decode(16, 1024) == 1
     assert L.int8_mixed_matmul_is_decode(17, 1024) == 0
-    assert L.int8_mixed_matmul_is_decode(8, 8192) == 0          # M*K above the LDS budget
+    # X chunks held per thread: rows held (M rounded up to a power of two) x K / 4096
+    assert L.int8_mixed_matmul_is_decode(16, 4096) == 1
+    assert L.int8_mixed_matmul_is_decode(9, 4112) == 0
+    assert L.int8_mixed_matmul_is_decode(8, 8192) == 1
+    assert L.int8_mixed_matmul_is_decode(8, 8208) == 0
+    assert L.int8_mixed_matmul_is_decode(4, 8192) == 1
     # prefill: at least Xq + a_x + Xo + WoT
     M, K, N, mo = 2048, 4096, 16384, 256
     b = ws(M, K, N, mo)

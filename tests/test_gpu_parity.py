@@ -164,10 +164,13 @@ def test_mixed_matmul_parity(M, K, N):
     check_y(Y, ref["Y"])
 
 
-# one shape per decode instantiation (rows held 2/4/8/16 x k-steps per wave 2/4/8/16)
+# one shape per decode instantiation (rows held 2/4/8/16 x k-steps per wave 2/4/8/16,
+# masked X staged in LDS), then the two without the staged copy (M = 16 from K = 2880,
+# M = 5..8 from K = 5536), at their largest shapes too
 DECODE_SHAPES = [(2, 528), (1, 2000), (2, 4000), (1, 8000), (3, 1008), (4, 1552), (3, 4080),
                  (4, 8192), (6, 992), (7, 2032), (5, 4096), (6, 5456), (12, 720), (11, 1792),
-                 (10, 3264)]
+                 (10, 3264),
+                 (7, 7008), (8, 8192), (13, 3600), (16, 4096)]
 
 
 @pytest.mark.parametrize("M,K", DECODE_SHAPES)
