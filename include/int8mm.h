@@ -121,8 +121,9 @@ size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_
  * Sums: int32 exact for the int8 part; the outlier part uses fp16 operands
  * (X values and Wq*w_absmax/127 rounded to fp16) with fp32 accumulation; the
  * epilogue combines both in fp32 and rounds once to fp16.
- * M <= 16, K <= 8192 and M*K <= 32768 run as one bandwidth-bound kernel; otherwise three
- * kernels (outlier mask, row quantization + outlier gathers, MFMA GEMM).
+ * M <= 16 with K <= 4096, and M <= 8 with K <= 8192, run as one bandwidth-bound kernel
+ * (int8_mixed_matmul_is_decode); otherwise three kernels (outlier mask, row
+ * quantization + outlier gathers, MFMA GEMM).
  */
 int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
