@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libint8mm.so")
-SOURCES = ["prepare.hip", "quant.hip", "gemm.hip", "decode.hip", "weight_only.hip", "int8mm_abi.hip"]
+SOURCES = ["prepare.hip", "quant.hip", "gemm.hip", "gemm_skinny.hip", "decode.hip", "weight_only.hip",
+           "int8mm_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

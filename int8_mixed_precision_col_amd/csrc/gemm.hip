@@ -31,8 +31,25 @@ static hipError_t run_grouped(GroupedGemmArgs& a, hipStream_t s, int group_m) {
   return hipGetLastError();
 }
 
-// Same choice of tile shape as launch_gemm, on the combined tile count.
+// Same choice of kernel and tile shape as launch_gemm, on the combined tile count. A
+// handful of tokens takes the skinny kernel once per weight: its blocks fill the GPU
+// at any width, and each output is then computed exactly as by the one-weight call.
 hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
+  bool skinny = true;
+  for (int q = 0; q < a.G; ++q) skinny = skinny && gemm_skinny_supported(a.base.M, a.N[q], a.base.K);
+  if (skinny) {
+    for (int q = 0; q < a.G; ++q) {
+      GemmArgs g = a.base;
+      g.Wq = a.Wq[q];
+      g.a_w = a.a_w[q];
+      g.WoT = a.WoT[q];
+      g.Y = a.Y[q];
+      g.N = a.N[q];
+      const hipError_t e = launch_gemm_skinny(g, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   long tiles_l = 0;
   for (int q = 0; q < a.G; ++q) tiles_l += static_cast<long>((a.N[q] + 255) / 256) * ((a.base.M + 255) / 256);
   if (a.base.M >= 256 && tiles_l >= 256) return run_grouped<CfgL>(a, s, 8);
@@ -40,6 +57,7 @@ hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (gemm_skinny_supported(g.M, g.N, g.K)) return launch_gemm_skinny(g, s);
   const long tiles_l = static_cast<long>((g.N + 255) / 256) * ((g.M + 255) / 256);
   if (g.M >= 256 && tiles_l >= 256) return run<CfgL>(g, s, 8);
   return run<CfgS>(g, s, 8);

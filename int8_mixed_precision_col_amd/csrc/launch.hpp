@@ -52,6 +52,10 @@ struct GemmArgs {
   int32_t* acc_out;     // nullable [M][N]
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// A handful of tokens: the weight-stream form of the same product (one block per 16
+// to 64 output features, all tokens), which launch_gemm picks for those shapes.
+bool gemm_skinny_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s);
 
 // Up to kMaxGroups weights sharing one activation state (base holds the shared fields;
 // its Wq, a_w, WoT, Y, N are unused).

@@ -150,6 +150,9 @@ CASES = [
     (300, 1040, 528), (17, 256, 4112), (64, 8192, 256), (1, 12288, 64),
     # prefill, large tiles
     (1040, 1040, 16400),
+    # prefill, weight-stream GEMM for a few tokens (token groups x feature groups per
+    # block: 1x1, 2x1, 3x1, 4x1, 2x2)
+    (9, 8208, 272), (24, 4096, 1040), (40, 2064, 1040), (64, 1024, 2064), (20, 1040, 32784),
 ]
 
 
@@ -162,6 +165,25 @@ def test_mixed_matmul_parity(M, K, N):
     ref, Y, acc = _mixed(X, W, 6.0, mo=min(256, K))
     assert np.array_equal(acc, ref["acc"])
     check_y(Y, ref["Y"])
+
+
+def test_largest_k_extreme_accumulators():
+    """K at the library's int32 guard (127^2 K < 2^31): a row of +1.0 and a row of -1.0
+    (every code +-127) against a weight column of 0.25 (every code 127) give the
+    largest sums the library admits, +-2 147 350 544, next to ordinary rows."""
+    M, K, N = 4, 133136, 32
+    announce(f"largest K M={M} K={K} N={N}")
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    X[0, :] = 1.0
+    X[1, :] = -1.0
+    W = weight(K + N, K, N)
+    W[:, 0] = 0.25
+    ref, Y, acc = _mixed(X, W, 6.0, mo=16)
+    assert ref["acc"][0, 0] == 127 * 127 * K and ref["acc"][1, 0] == -127 * 127 * K
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+    check_y(Y[2:], ref["Y"][2:])
 
 
 # one shape per decode instantiation (rows held 2/4/8/16 x k-steps per wave 2/4/8/16,
@@ -310,7 +332,7 @@ def test_weight_only_parity(M, K, N):
 
 
 @pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
-                                    (64, 8192, (256,))])
+                                    (64, 8192, (256,)), (5, 1024, (32784, 65552))])
 def test_quantize_once_feeds_several_weights(M, K, Ns):
     """One activation quantization, several weights: each product equals the oracle
     (acc bit-exact, Y within tolerance) and, on the multi-kernel path, the one-call
@@ -337,10 +359,14 @@ def test_quantize_once_feeds_several_weights(M, K, Ns):
 
 @pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
                                     (2048, 1024, (4096, 4096, 4096)),
-                                    (257, 528, (16, 48, 80, 272, 528, 16, 32, 64))])
+                                    (257, 528, (16, 48, 80, 272, 528, 16, 32, 64)),
+                                    (40, 1040, (528, 65536))])
 def test_grouped_launch_equals_per_weight_calls(M, K, Ns):
     """One grouped GEMM launch over several weights: every output equals the
-    one-weight int8_mixed_matmul_q call bit for bit (small- and large-tile grids)."""
+    one-weight int8_mixed_matmul_q call bit for bit (small- and large-tile grids, and
+    the weight-stream kernel). In the last case the 68 MB weight sends the grouped call
+    to the 128 x 128 tiles while the one-weight call of the small weight takes the
+    weight-stream kernel: the two kernels' outputs are compared bit for bit."""
     announce(f"grouped launch M={M} K={K} Ns={Ns}")
     X = planted(M + K + len(Ns), M, K, n_dims=3)
     state = binding.QuantizedActivations(dev(X), 6.0, 64)
