@@ -123,7 +123,10 @@ size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_
  * epilogue combines both in fp32 and rounds once to fp16.
  * M <= 16 with K <= 4096, and M <= 8 with K <= 8192, run as one bandwidth-bound kernel
  * (int8_mixed_matmul_is_decode); otherwise three kernels (outlier mask, row
- * quantization + outlier gathers, MFMA GEMM).
+ * quantization + outlier gathers, MFMA GEMM). The GEMM is tiled (256 x 256 or 128 x 128
+ * outputs per block) or, for a few tokens (M <= 32, or M <= 64 with N K <= 2^26; K >=
+ * 1024), a weight stream with one block per 16-64 output features; both compute every
+ * output with the same arithmetic, so Y does not depend on which one runs.
  */
 int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
@@ -162,7 +165,8 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
                         hipStream_t stream);
 
 /*
- * int8_mixed_matmul_q for G <= 8 weights at once, in one GEMM launch: the weights'
+ * int8_mixed_matmul_q for G <= 8 weights at once, in one GEMM launch (for a few
+ * tokens, where the weight-stream kernel fills the GPU by itself, one per weight): the weights'
  * output tiles form one grid, so projections too narrow to fill the GPU on their
  * own (Q, K, V of one layer) run side by side ([Abstract]: the attention and
  * feed-forward projection layers share the input the state was made from).

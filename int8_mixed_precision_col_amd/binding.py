@@ -248,7 +248,7 @@ class QuantizedActivations:
     def matmul_grouped(self, weights: list, outs: list | None = None,
                        workspace: torch.Tensor | None = None) -> list:
         """Y fp16 [M, N_q] for each (Wq, a_w) in `weights` (at most 8), from this
-        quantized X, in one GEMM launch."""
+        quantized X, in one GEMM launch (one per weight for a few tokens)."""
         G = len(weights)
         Ns = []
         for Wq, a_w in weights:
