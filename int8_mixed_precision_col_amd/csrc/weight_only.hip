@@ -9,10 +9,11 @@
 // Wq[n, k] a_w[n] / 127, with fp32 accumulation; the constant is applied once per
 // output.
 //
-// One block per 16 output features (one 16-row group of the unit-tiled Wq), 16 waves.
+// One block per 16 RG output features (RG 16-row groups of the unit-tiled Wq; RG = 2
+// where N leaves more than 2048 blocks of 16, so that fewer blocks re-read X), 16 waves.
 // Wave w takes k-steps w, w + 16, ... (64 columns each) in batches of kWoBatch; per
 // step every lane loads one 16-byte slice of the step's 1 KB weight unit and the two
-// 8-column pieces of X (its token, the same columns) that the MFMA pairs with it,
+// 8-column pieces of X (its token, the same columns) that the MFMAs pair with it,
 // straight into registers: no staging, no barrier before the products. X loads go
 // through a buffer resource, so tokens past M and columns past K read zeros without
 // touching memory. The int8 bytes become exact fp16 values (1024 + (q + 128) built
@@ -40,14 +41,19 @@ __device__ __forceinline__ v2u int8x4_to_half(unsigned d) {
   return o;
 }
 
+template <int RG>
 __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a) {
-  __shared__ float red[kWoWaves][16][17];
-  const int K = a.K, M = a.M;
+  __shared__ float red[kWoWaves][16 * RG][17];
+  const int K = a.K, M = a.M, N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * RG;
   const int ks = unit_ks(K);
   const int g = lane >> 4, tok = lane & 15;
-  const int8_t* wunit = a.Wq + static_cast<size_t>(n0 >> 4) * ks * kUnitBytes + (lane & 15) * kUnitK + 16 * g;
+  const int8_t* wunit[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+    wunit[r] = a.Wq + static_cast<size_t>(min(n0 / 16 + r, N / 16 - 1)) * ks * kUnitBytes +
+               (lane & 15) * kUnitK + 16 * g;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, static_cast<unsigned>(M) * K * 2u);
   // byte offset of this lane's X piece at k-step s (K is a multiple of 16: a 16-column
   // piece is either inside the row or past it); out of range past M or K
@@ -55,47 +61,57 @@ __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a)
     const int k = 64 * s + 16 * g;
     return tok < M && k < K ? static_cast<unsigned>(tok * K + k) * 2u : kOOB;
   };
-  v4u wf[kWoBatch], x0[kWoBatch], x1[kWoBatch];
+  v4u wf[kWoBatch][RG], x0[kWoBatch], x1[kWoBatch];
   auto load_batch = [&](int base) {
 #pragma unroll
     for (int j = 0; j < kWoBatch; ++j) {
       const int s = base + kWoWaves * j;
-      wf[j] = *reinterpret_cast<const v4u*>(wunit + static_cast<size_t>(s < ks ? s : 0) * kUnitBytes);
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+        wf[j][r] = *reinterpret_cast<const v4u*>(wunit[r] + static_cast<size_t>(s < ks ? s : 0) * kUnitBytes);
       const unsigned o = s < ks ? x_off(s) : kOOB;
       x0[j] = buf_load16(xr, o);
       x1[j] = buf_load16(xr, o == kOOB ? kOOB : o + 16u);
     }
   };
   load_batch(wave);
-  const float aw_pre = a.a_w[n0 + (tid & 15)];  // epilogue constant, loaded early
+  // this thread's output (token m, feature n0 + nl) and its constant, loaded early
+  const int m = tid / (16 * RG), nl = tid % (16 * RG), n = n0 + nl;
+  const float aw_pre = a.a_w[min(n, N - 1)];
 
-  v4f acc = v4f{};
+  v4f acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = v4f{};
   for (int base = wave;;) {
 #pragma unroll
     for (int j = 0; j < kWoBatch; ++j) {
       if (base + kWoWaves * j < ks) {  // wave-uniform
-        const v2u h0 = int8x4_to_half(wf[j][0]), h1 = int8x4_to_half(wf[j][1]);
-        const v2u h2 = int8x4_to_half(wf[j][2]), h3 = int8x4_to_half(wf[j][3]);
-        const v4u wa = {h0[0], h0[1], h1[0], h1[1]};
-        const v4u wb = {h2[0], h2[1], h3[0], h3[1]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, wa), __builtin_bit_cast(v8h, x0[j]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, wb), __builtin_bit_cast(v8h, x1[j]), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const v2u h0 = int8x4_to_half(wf[j][r][0]), h1 = int8x4_to_half(wf[j][r][1]);
+          const v2u h2 = int8x4_to_half(wf[j][r][2]), h3 = int8x4_to_half(wf[j][r][3]);
+          const v4u wa = {h0[0], h0[1], h1[0], h1[1]};
+          const v4u wb = {h2[0], h2[1], h3[0], h3[1]};
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, wa), __builtin_bit_cast(v8h, x0[j]), acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, wb), __builtin_bit_cast(v8h, x1[j]), acc[r], 0, 0, 0);
+        }
       }
     }
     base += kWoWaves * kWoBatch;
     if (base >= ks) break;
     load_batch(base);
   }
-  // 16x16 accumulator layout: lane l, register r -> column (token) l % 16, row 4 (l / 16) + r
+  // 16x16 accumulator layout: lane l, register e -> column (token) l % 16, row 4 (l / 16) + e
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][4 * g + r][tok] = acc[r];
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][16 * r + 4 * g + e][tok] = acc[r][e];
   lds_barrier();
-  const int m = tid >> 4, nl = tid & 15, n = n0 + nl;
-  if (m < M) {
+  if (m < M && n < N) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWoWaves; ++w) s += red[w][nl][m];
-    a.Y[static_cast<size_t>(m) * a.N + n] = static_cast<_Float16>(s * __fdiv_rn(aw_pre, 127.0f));
+    a.Y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(s * __fdiv_rn(aw_pre, 127.0f));
   }
 }
 
@@ -105,7 +121,12 @@ bool weight_only_supported(int64_t M, int64_t K) {
 }
 
 hipError_t launch_weight_only(const WeightOnlyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_weight_only, dim3(a.N / 16), dim3(64 * kWoWaves), 0, s, a);
+  const int nrg = a.N / 16;
+  if (nrg > 2048) {
+    hipLaunchKernelGGL(k_weight_only<2>, dim3((nrg + 1) / 2), dim3(64 * kWoWaves), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_weight_only<1>, dim3(nrg), dim3(64 * kWoWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -318,7 +318,9 @@ def test_graph_replay_matches_eager(M, K, N):
 
 @pytest.mark.parametrize("M,K,N", [(8, 4096, 4096), (1, 32, 16), (16, 1040, 528),
                                    (5, 12288, 64), (3, 16, 48), (16, 12288, 272),
-                                   (7, 20480, 48), (12, 5136, 16)])
+                                   (7, 20480, 48), (12, 5136, 16),
+                                   # 32 features per block, odd count of 16-feature groups
+                                   (3, 1040, 32784), (16, 528, 34816)])
 def test_weight_only_parity(M, K, N):
     """Weight-only int8 (no activation quantization) against the oracle's fp16(X @ W^)."""
     announce(f"weight-only M={M} K={K} N={N}")
