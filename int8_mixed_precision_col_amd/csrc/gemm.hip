@@ -42,7 +42,6 @@ hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
       GemmArgs g = a.base;
       g.Wq = a.Wq[q];
       g.a_w = a.a_w[q];
-      g.WoT = a.WoT[q];
       g.Y = a.Y[q];
       g.N = a.N[q];
       const hipError_t e = launch_gemm_skinny(g, s);

@@ -6,8 +6,9 @@
 // Y[m, n]   = fp16( acc * a_x[m] * a_w[n] / 127^2              (outer-product dequant,
 //                   "8-bit Matrix Multiplication for Large Language Models", Summary &
 //                   Methodology Analysis)
-//                 + sum_r Xo[m, r] WoT[n, r] )                  (16-bit product over the
-//                   outlier columns, summed into the same fp16 output)
+//                 + sum_r Xo[m, r] W^[O_r, n] )                 (16-bit product over the
+//                   outlier columns O_r, summed into the same fp16 output; W^ is the
+//                   int8 weight dequantized, fp16(Wq a_w / 127))
 //
 // gfx950 design. Both operands are K-contiguous, so a block computes D = Wq_tile *
 // Xq_tile^T with v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with 16 consecutive K
@@ -25,11 +26,13 @@
 // reads are free of bank conflicts. Slab kt + STAGES - 1 is in
 // flight while slab kt is multiplied; one barrier per slab.
 // The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, with the
-// small Xo / WoT fragments staged through LDS, accumulating on top of the already
+// small Xo / W^ fragments staged through LDS (W^ dequantized from the Wq bytes of the
+// outlier columns as they are staged), accumulating on top of the already
 // dequantized fp32 values before the single rounding to fp16.
 #pragma once
 
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "launch.hpp"
 
 namespace i8mm {
@@ -130,7 +133,7 @@ __device__ __forceinline__ char* stage_buf() {
 
 // Epilogue. 32x32 accumulator layout: lane l, register r holds column m = l % 32 and
 // row n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). The tile's
-// a_w / a_x and the outlier fragments (16 columns of WoT and Xo per pass) are staged
+// a_w / a_x and the outlier fragments (16 columns of W^ and Xo per pass) are staged
 // in stage 0 of the ring first (free once the K loop is done), so that no global
 // load waits inside the per-block loops; reading them straight from global memory,
 // one block of 32 x 32 at a time, took ~13 us per tile against ~8 us now. Per block:
@@ -151,13 +154,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   const int count = *g.count;
   const bool overflow = count > g.max_outliers;
   const int o_pad = min((count + 15) & ~15, g.o_stride);
-  const int M = g.M, N = g.N;
+  const int nvalid = min(count, g.max_outliers);
+  const int M = g.M, N = g.N, ks = unit_ks(g.K);
   auto stage_outliers = [&](int s0) {
     for (int t = tid; t < (C::TN + C::TM) * 2; t += C::NT) {
       const int row = t >> 1, h = t & 1;
       if (row < C::TN)
-        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) = *reinterpret_cast<const v8h*>(
-            g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h);
+        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
+            outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
       else
         *reinterpret_cast<v8h*>(xo_s + (row - C::TN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
             g.Xo + static_cast<size_t>(min(m0 + row - C::TN, M - 1)) * g.o_stride + s0 + 8 * h);
@@ -461,7 +465,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm_grouped(GroupedGemmArgs ga, int 
   GemmArgs g = ga.base;
   g.Wq = ga.Wq[q];
   g.a_w = ga.a_w[q];
-  g.WoT = ga.WoT[q];
   g.Y = ga.Y[q];
   g.N = ga.N[q];
   gemm_tile<C>(g, tnv - ga.tn_first[q], tm);

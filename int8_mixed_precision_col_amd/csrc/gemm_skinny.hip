@@ -16,9 +16,11 @@
 // while this one multiplies. The waves' int32 partials are summed exactly through LDS.
 // The epilogue is k_gemm's: per 32 x 32 block of (feature, token), dequantize in fp32
 // as acc * (a_x * 1/127^2) * a_w, add the outlier product with v_mfma_f32_32x32x16_f16
-// over the same 16-column chunks of Xo and WoT in the same order, round once to fp16;
+// over the same 16-column chunks of Xo and the dequantized outlier weights in the same
+// order, round once to fp16;
 // so Y is bit-identical to k_gemm's for the same inputs.
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "launch.hpp"
 
 namespace i8mm {
@@ -120,15 +122,17 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
   const int count = *g.count;
   const bool overflow = count > g.max_outliers;
   const int o_pad = min((count + 15) & ~15, g.o_stride);
+  const int nvalid = min(count, g.max_outliers);
   for (int t = tid; t < 32 * EN; t += kSkThreads) aw_s[t] = g.a_w[min(n0 + t, N - 1)];
   for (int t = tid; t < 32 * EM; t += kSkThreads) ax_s[t] = g.a_x[min(t, M - 1)];
-  // the outlier columns s0 .. s0 + 15 of the block's WoT rows and of Xo
+  // the outlier columns s0 .. s0 + 15: the block's weight rows (dequantized from Wq)
+  // and Xo
   auto stage_outliers = [&](int s0) {
     for (int t = tid; t < 32 * (EN + EM) * 2; t += kSkThreads) {
       const int row = t >> 1, h = t & 1;
       if (row < 32 * EN)
-        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) = *reinterpret_cast<const v8h*>(
-            g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h);
+        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
+            outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
       else
         *reinterpret_cast<v8h*>(xo_s + (row - 32 * EN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
             g.Xo + static_cast<size_t>(min(row - 32 * EN, M - 1)) * g.o_stride + s0 + 8 * h);

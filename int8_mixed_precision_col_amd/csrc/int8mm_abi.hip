@@ -37,14 +37,16 @@ int mask_row_chunks(int64_t M, int64_t K) {
 }
 
 struct Layout {
-  size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, wot = 0, total = 0;
+  size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, idx = 0, total = 0;
   int R = 1, o_stride = 0;
 };
 
 // Workspace: [status, count] header, then (prefill only) the row-chunk column flags,
-// a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and WoT, each 256-byte aligned.
-// A quantized-activation state (int8_quantize_activations) is the same without WoT.
-Layout prefill_layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+// a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and the ascending outlier column
+// list, each 256-byte aligned. A quantized-activation state (int8_quantize_activations)
+// has the same layout; neither depends on N (the GEMM epilogue dequantizes the outlier
+// columns' weights from Wq itself).
+Layout prefill_layout(int64_t M, int64_t K, int64_t max_outliers) {
   Layout L;
   size_t off = 256;
   const size_t W = (K + 31) / 32;
@@ -55,19 +57,22 @@ Layout prefill_layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   L.a_x = off;     off += round256(size_t(M) * 4);
   L.xq = off;      off += round256(m_rows * i8mm::unit_ks(int(K)) * i8mm::kUnitK);
   L.xo = off;      off += round256(size_t(M) * L.o_stride * 2);
-  L.wot = off;     off += round256(size_t(N) * L.o_stride * 2);
+  L.idx = off;     off += round256(size_t(max_outliers) * 4);
   L.total = off;
   return L;
 }
 
-Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
+Layout layout(int64_t M, int64_t K, int64_t max_outliers) {
   if (i8mm::decode_supported(M, K)) {
     Layout L;
     L.total = 256;
     return L;
   }
-  return prefill_layout(M, K, N, max_outliers);
+  return prefill_layout(M, K, max_outliers);
 }
+
+// The weight side needs no scratch: a fixed, reserved size.
+constexpr size_t kQWorkspaceBytes = 256;
 
 // Optional event timing of the main kernel.
 bool g_timing = false;
@@ -137,7 +142,7 @@ size_t int8_prepared_weight_bytes(int64_t K, int64_t N) {
 
 size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return 0;
-  return layout(M, K, N, max_outliers).total;
+  return layout(M, K, max_outliers).total;
 }
 
 int int8_mixed_matmul_is_decode(int64_t M, int64_t K) {
@@ -154,7 +159,7 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
       !aligned16(workspace) || (acc_i32 && !aligned16(acc_i32)))
     return INT8MM_E_ALIGN;
-  const Layout L = layout(M, K, N, max_outliers);
+  const Layout L = layout(M, K, max_outliers);
   if (workspace_bytes < L.total) return INT8MM_E_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
@@ -178,7 +183,7 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   float* a_x = reinterpret_cast<float*>(ws + L.a_x);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
   _Float16* xo = reinterpret_cast<_Float16*>(ws + L.xo);
-  _Float16* wot = reinterpret_cast<_Float16*>(ws + L.wot);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
 
   if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
     return INT8MM_E_HIP;
@@ -186,16 +191,15 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   q.X = x; q.M = int(M); q.K = int(K);
   q.partial = partial; q.R = L.R;
   q.Xq = xq; q.xq_tiled = 1; q.a_x = a_x;
-  q.idx_out = nullptr; q.count_out = status + 1; q.status_out = status;
+  q.idx_out = max_outliers > 0 ? idx : nullptr; q.count_out = status + 1; q.status_out = status;
   q.max_outliers = int(max_outliers);
   q.Xo = xo; q.o_stride = L.o_stride;
-  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
   if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
 
   i8mm::GemmArgs g{};
   g.Wq = Wq; g.Xq = xq; g.M = int(M); g.N = int(N); g.K = int(K);
   g.a_x = a_x; g.a_w = w_absmax;
-  g.Xo = xo; g.WoT = wot; g.o_stride = L.o_stride;
+  g.Xo = xo; g.idx = idx; g.o_stride = L.o_stride;
   g.count = status + 1; g.max_outliers = int(max_outliers);
   g.Y = y; g.acc_out = acc_i32;
   if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;
@@ -205,13 +209,12 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
 
 size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers) {
   if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return 0;
-  return prefill_layout(M, K, 0, max_outliers).wot;  // everything before WoT
+  return prefill_layout(M, K, max_outliers).total;
 }
 
 size_t int8_mixed_matmul_q_workspace_bytes(int64_t N, int64_t max_outliers) {
   if (bad_n(N) || max_outliers < 0 || max_outliers > kMaxOutliers) return 0;
-  const size_t o_stride = (max_outliers + 15) & ~int64_t(15);
-  return round256(size_t(N) * o_stride * 2 + 16);
+  return kQWorkspaceBytes;
 }
 
 int int8_quantize_activations(const void* X, int64_t M, int64_t K, float threshold,
@@ -221,8 +224,8 @@ int int8_quantize_activations(const void* X, int64_t M, int64_t K, float thresho
   if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
   if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
   if (!aligned16(X) || !aligned16(state)) return INT8MM_E_ALIGN;
-  const Layout L = prefill_layout(M, K, 0, max_outliers);
-  if (state_bytes < L.wot) return INT8MM_E_WORKSPACE;
+  const Layout L = prefill_layout(M, K, max_outliers);
+  if (state_bytes < L.total) return INT8MM_E_WORKSPACE;
   char* ws = static_cast<char*>(state);
   int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
   const _Float16* x = static_cast<const _Float16*>(X);
@@ -234,10 +237,10 @@ int int8_quantize_activations(const void* X, int64_t M, int64_t K, float thresho
   q.partial = partial; q.R = L.R;
   q.Xq = reinterpret_cast<int8_t*>(ws + L.xq); q.xq_tiled = 1;
   q.a_x = reinterpret_cast<float*>(ws + L.a_x);
-  q.idx_out = nullptr; q.count_out = status + 1; q.status_out = status;
+  q.idx_out = max_outliers > 0 ? reinterpret_cast<int32_t*>(ws + L.idx) : nullptr;
+  q.count_out = status + 1; q.status_out = status;
   q.max_outliers = int(max_outliers);
   q.Xo = reinterpret_cast<_Float16*>(ws + L.xo); q.o_stride = L.o_stride;
-  q.WoT = nullptr;
   return hip_status(i8mm::launch_quant_rows(q, stream));
 }
 
@@ -252,25 +255,15 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
     return INT8MM_E_ALIGN;
   if (workspace_bytes < int8_mixed_matmul_q_workspace_bytes(N, max_outliers))
     return INT8MM_E_WORKSPACE;
-  const Layout L = prefill_layout(M, K, N, max_outliers);
+  const Layout L = prefill_layout(M, K, max_outliers);
   const char* st = static_cast<const char*>(state);
   const int32_t* status = reinterpret_cast<const int32_t*>(st + L.status);
-  _Float16* wot = static_cast<_Float16*>(workspace);
-  // the weight-specific part of the outlier product: dequantized outlier rows of Wq
-  i8mm::QuantRowsArgs q{};
-  q.M = int(M); q.K = int(K);
-  q.partial = reinterpret_cast<const uint32_t*>(st + L.partial); q.R = L.R;
-  q.gather_only = 1;
-  q.count_out = nullptr; q.status_out = nullptr; q.idx_out = nullptr;
-  q.max_outliers = int(max_outliers);
-  q.o_stride = L.o_stride;
-  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
-  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
   i8mm::GemmArgs g{};
   g.Wq = Wq; g.Xq = reinterpret_cast<const int8_t*>(st + L.xq); g.M = int(M); g.N = int(N);
   g.K = int(K);
   g.a_x = reinterpret_cast<const float*>(st + L.a_x); g.a_w = w_absmax;
-  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo); g.WoT = wot; g.o_stride = L.o_stride;
+  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo);
+  g.idx = reinterpret_cast<const int32_t*>(st + L.idx); g.o_stride = L.o_stride;
   g.count = status + 1; g.max_outliers = int(max_outliers);
   g.Y = static_cast<_Float16*>(Y); g.acc_out = acc_i32;
   int rc;
@@ -307,31 +300,19 @@ int int8_mixed_matmul_q_grouped(const void* state, int64_t M, int64_t K, int64_t
     if (!aligned16(Wq[q]) || !aligned16(w_absmax[q]) || !aligned16(Y[q])) return INT8MM_E_ALIGN;
   if (workspace_bytes < int8_mixed_matmul_q_grouped_workspace_bytes(G, N, max_outliers))
     return INT8MM_E_WORKSPACE;
-  const Layout L = prefill_layout(M, K, 0, max_outliers);
+  const Layout L = prefill_layout(M, K, max_outliers);
   const char* st = static_cast<const char*>(state);
   const int32_t* status = reinterpret_cast<const int32_t*>(st + L.status);
   i8mm::GroupedGemmArgs ga{};
   i8mm::GemmArgs& g = ga.base;
   g.Xq = reinterpret_cast<const int8_t*>(st + L.xq); g.M = int(M); g.K = int(K);
   g.a_x = reinterpret_cast<const float*>(st + L.a_x);
-  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo); g.o_stride = L.o_stride;
+  g.Xo = reinterpret_cast<const _Float16*>(st + L.xo);
+  g.idx = reinterpret_cast<const int32_t*>(st + L.idx); g.o_stride = L.o_stride;
   g.count = status + 1; g.max_outliers = int(max_outliers); g.acc_out = nullptr;
   ga.G = int(G);
-  char* ws = static_cast<char*>(workspace);
   for (int64_t q = 0; q < G; ++q) {
-    // each weight's dequantized outlier rows, gathered from the shared outlier list
-    _Float16* wot = reinterpret_cast<_Float16*>(ws);
-    ws += int8_mixed_matmul_q_workspace_bytes(N[q], max_outliers);
-    i8mm::QuantRowsArgs qa{};
-    qa.M = int(M); qa.K = int(K);
-    qa.partial = reinterpret_cast<const uint32_t*>(st + L.partial); qa.R = L.R;
-    qa.gather_only = 1;
-    qa.count_out = nullptr; qa.status_out = nullptr; qa.idx_out = nullptr;
-    qa.max_outliers = int(max_outliers);
-    qa.o_stride = L.o_stride;
-    qa.Wq = Wq[q]; qa.a_w = w_absmax[q]; qa.N = int(N[q]); qa.WoT = wot;
-    if (i8mm::launch_quant_rows(qa, stream) != hipSuccess) return INT8MM_E_HIP;
-    ga.Wq[q] = Wq[q]; ga.a_w[q] = w_absmax[q]; ga.WoT[q] = wot;
+    ga.Wq[q] = Wq[q]; ga.a_w[q] = w_absmax[q];
     ga.Y[q] = static_cast<_Float16*>(Y[q]); ga.N[q] = int(N[q]);
   }
   int rc;

@@ -23,17 +23,13 @@ struct QuantRowsArgs {
   int8_t* Xq;
   int xq_tiled;         // 0: Xq row-major [M][K]; 1: unit-tiled (GEMM operand layout)
   float* a_x;
-  int32_t* idx_out;     // [max_outliers], nullable when max_outliers == 0
+  int32_t* idx_out;     // [max_outliers] ascending outlier columns (the first
+                        // min(count, max_outliers)), nullable
   int32_t* count_out;   // [1]
   int32_t* status_out;  // [1], nullable
   int max_outliers;
   _Float16* Xo;         // nullable: [M][o_stride] fp16 outlier activations
   int o_stride;         // multiple of 16, >= max_outliers
-  const int8_t* Wq;     // unit-tiled, for the WoT gather (nullable = no gather)
-  const float* a_w;
-  int N;
-  _Float16* WoT;        // [N][o_stride] fp16 dequantized outlier weight rows
-  int gather_only;      // 1: no row blocks (X, Xq, a_x, Xo unused; count_out may be null)
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
 
@@ -44,7 +40,7 @@ struct GemmArgs {
   const float* a_x;
   const float* a_w;
   const _Float16* Xo;   // [M][o_stride]
-  const _Float16* WoT;  // [N][o_stride]
+  const int32_t* idx;   // ascending outlier columns, the first min(count, max_outliers) valid
   int o_stride;
   const int32_t* count;
   int max_outliers;
@@ -58,14 +54,13 @@ bool gemm_skinny_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s);
 
 // Up to kMaxGroups weights sharing one activation state (base holds the shared fields;
-// its Wq, a_w, WoT, Y, N are unused).
+// its Wq, a_w, Y, N are unused).
 constexpr int kMaxGroups = 8;
 struct GroupedGemmArgs {
   GemmArgs base;
   int G;
   const int8_t* Wq[kMaxGroups];
   const float* a_w[kMaxGroups];
-  const _Float16* WoT[kMaxGroups];
   _Float16* Y[kMaxGroups];
   int N[kMaxGroups];
   int tn_first[kMaxGroups + 1];  // first virtual tile column of each group (filled by the launcher)
