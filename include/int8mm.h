@@ -150,7 +150,8 @@ int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
  *                 written by int8_quantize_activations, read by int8_mixed_matmul_q;
  *                 it holds the status word (int8mm_read_status works on it).
  *   workspace     (int8_mixed_matmul_q) at least int8_mixed_matmul_q_workspace_bytes(N,
- *                 max_outliers) bytes: the weight's dequantized outlier rows.
+ *                 max_outliers) bytes, a fixed 256: reserved (the weight side needs no
+ *                 scratch; the GEMM dequantizes the outlier columns' weights itself).
  * M, K, max_outliers and the threshold's outcome are those of the quantization
  * call; arguments are validated as for int8_mixed_matmul.
  */
@@ -175,7 +176,7 @@ int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_out
  *                 each weight's unit-tiled int8 matrix, fp32 [N[q]] constants, output
  *                 width (multiple of 16) and fp16 output [M, N[q]].
  *   workspace     at least int8_mixed_matmul_q_grouped_workspace_bytes(G, N,
- *                 max_outliers) bytes (the weights' outlier rows, one after another).
+ *                 max_outliers) bytes (reserved, 256 per weight).
  * Each Y[q] equals int8_mixed_matmul_q's output for that weight bit for bit. No
  * int32 sums output. Errors as for int8_mixed_matmul_q; G out of range or a bad
  * N[q] is INT8MM_E_SHAPE, a null entry INT8MM_E_NULL.
