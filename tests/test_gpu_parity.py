@@ -148,8 +148,9 @@ CASES = [
     (4, 8192, 256), (3, 8176, 48), (9, 3600, 144),
     # prefill, small tiles
     (300, 1040, 528), (17, 256, 4112), (64, 8192, 256), (1, 12288, 64),
-    # prefill, large tiles
-    (1040, 1040, 16400),
+    # prefill, tile shapes the launcher picks: 128 x 128 (many tiles), 256 x 256,
+    # 128 x 256
+    (1040, 1040, 16400), (385, 1040, 16608), (129, 1040, 16608),
     # prefill, weight-stream GEMM for a few tokens (token groups x feature groups per
     # block: 1x1, 2x1, 3x1, 4x1, 2x2)
     (9, 8208, 272), (24, 4096, 1040), (40, 2064, 1040), (64, 1024, 2064), (20, 1040, 32784),
