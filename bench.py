@@ -53,7 +53,7 @@ def array_digest(a: np.ndarray) -> str:
 
 
 KERNEL_SOURCES = {
-    "k_gemm": ("gemm.hip", "gemm_kernel.hpp", "common.hpp"),
+    "k_gemm": ("gemm.hip", "gemm_kernel.hpp", "epilogue.hpp", "launch.hpp", "common.hpp"),
     "k_decode": ("decode.hip", "common.hpp"),
 }
 COPY_PROBE_BYTES = 1 << 30   # plain copy kernel of known size for counter scaling

@@ -6,7 +6,8 @@
 
 namespace i8mm {
 
-// The weights of outlier ranks r0 .. r0 + 7 in output row n, dequantized from the int8
+// The weights of outlier ranks r0 .. r0 + 7 in output row n (the same values as the
+// gathered rows WoT of the one-call path, by the same expression), dequantized from the int8
 // copy that is the only weight kept in memory: fp16(Wq[n, O_r] a_w[n] / 127) ("LLM.int8():
 // 8-bit Matrix Multiplication for Transformers at Scale", Abstract: the weights are
 // converted to Int8 at load; the outlier columns are multiplied in 16 bit). Ranks from

@@ -49,7 +49,10 @@ template <class C>
 static hipError_t run(const GemmArgs& g, hipStream_t s, int group_m) {
   const int tiles_n = (g.N + C::TN - 1) / C::TN, tiles_m = (g.M + C::TM - 1) / C::TM;
   if (group_m > tiles_m) group_m = tiles_m;
-  hipLaunchKernelGGL(k_gemm<C>, dim3(tiles_n * tiles_m), dim3(C::NT), 0, s, g, tiles_m, group_m);
+  if (g.WoT)
+    hipLaunchKernelGGL((k_gemm<C, false>), dim3(tiles_n * tiles_m), dim3(C::NT), 0, s, g, tiles_m, group_m);
+  else
+    hipLaunchKernelGGL((k_gemm<C, true>), dim3(tiles_n * tiles_m), dim3(C::NT), 0, s, g, tiles_m, group_m);
   return hipGetLastError();
 }
 

@@ -26,8 +26,9 @@
 // reads are free of bank conflicts. Slab kt + STAGES - 1 is in
 // flight while slab kt is multiplied; one barrier per slab.
 // The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, with the
-// small Xo / W^ fragments staged through LDS (W^ dequantized from the Wq bytes of the
-// outlier columns as they are staged), accumulating on top of the already
+// small Xo / W^ fragments staged through LDS (W^ gathered beforehand, or dequantized
+// from the Wq bytes of the outlier columns as they are staged), accumulating on top of
+// the already
 // dequantized fp32 values before the single rounding to fp16.
 #pragma once
 
@@ -139,7 +140,7 @@ __device__ __forceinline__ char* stage_buf() {
 // one block of 32 x 32 at a time, took ~13 us per tile against ~8 us now. Per block:
 // store the int32 sums if asked, dequantize in place to fp32, let the fp16 outlier
 // MFMA accumulate on top of that, round once to fp16.
-template <class C>
+template <class C, bool GATHER>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::BN][C::BM],
                                                      int n0, int m0, int wn, int wm, int lane,
                                                      int tid) {
@@ -159,10 +160,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   auto stage_outliers = [&](int s0) {
     for (int t = tid; t < (C::TN + C::TM) * 2; t += C::NT) {
       const int row = t >> 1, h = t & 1;
-      if (row < C::TN)
-        *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
-            outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
-      else
+      if (row < C::TN) {
+        if constexpr (GATHER)
+          *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
+              outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
+        else
+          *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) = *reinterpret_cast<const v8h*>(
+              g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h);
+      } else
         *reinterpret_cast<v8h*>(xo_s + (row - C::TN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
             g.Xo + static_cast<size_t>(min(m0 + row - C::TN, M - 1)) * g.o_stride + s0 + 8 * h);
     }
@@ -376,8 +381,9 @@ struct GemmBlock {
 };
 
 // One output tile (tn, tm) of the product described by g: the whole K loop and the
-// epilogue.
-template <class C>
+// epilogue. GATHER: the outlier columns' weights are dequantized from Wq in the
+// epilogue (g.WoT unused); otherwise they are read from the gathered rows g.WoT.
+template <class C, bool GATHER>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
   GemmBlock<C> b{g};
   const int tid = threadIdx.x;
@@ -440,14 +446,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
   }
   // no DMA may still be writing this block's LDS when the block exits
   __builtin_amdgcn_s_waitcnt(0);
-  gemm_epilogue<C>(g, b.acc, n0, m0, b.wn, b.wm, b.lane, tid);
+  gemm_epilogue<C, GATHER>(g, b.acc, n0, m0, b.wn, b.wm, b.lane, tid);
 }
 
-template <class C>
+template <class C, bool GATHER>
 __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int group_m) {
   int tn, tm;
   tile_of(blockIdx.x, gridDim.x, tiles_m, group_m, tn, tm);
-  gemm_tile<C>(g, tn, tm);
+  gemm_tile<C, GATHER>(g, tn, tm);
 }
 
 // Several weights against one quantized activation in one launch: the groups' column
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm_grouped(GroupedGemmArgs ga, int 
   g.a_w = ga.a_w[q];
   g.Y = ga.Y[q];
   g.N = ga.N[q];
-  gemm_tile<C>(g, tnv - ga.tn_first[q], tm);
+  gemm_tile<C, true>(g, tnv - ga.tn_first[q], tm);
 }
 
 #undef I8MM_LDS

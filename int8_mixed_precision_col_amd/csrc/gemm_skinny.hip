@@ -125,14 +125,15 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
   const int nvalid = min(count, g.max_outliers);
   for (int t = tid; t < 32 * EN; t += kSkThreads) aw_s[t] = g.a_w[min(n0 + t, N - 1)];
   for (int t = tid; t < 32 * EM; t += kSkThreads) ax_s[t] = g.a_x[min(t, M - 1)];
-  // the outlier columns s0 .. s0 + 15: the block's weight rows (dequantized from Wq)
-  // and Xo
+  // the outlier columns s0 .. s0 + 15: the block's weight rows (gathered beforehand, or
+  // dequantized from Wq) and Xo
   auto stage_outliers = [&](int s0) {
     for (int t = tid; t < 32 * (EN + EM) * 2; t += kSkThreads) {
       const int row = t >> 1, h = t & 1;
       if (row < 32 * EN)
         *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
-            outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
+            g.WoT ? *reinterpret_cast<const v8h*>(g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h)
+                  : outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
       else
         *reinterpret_cast<v8h*>(xo_s + (row - 32 * EN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
             g.Xo + static_cast<size_t>(min(row - 32 * EN, M - 1)) * g.o_stride + s0 + 8 * h);

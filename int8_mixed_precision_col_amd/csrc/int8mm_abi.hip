@@ -37,15 +37,16 @@ int mask_row_chunks(int64_t M, int64_t K) {
 }
 
 struct Layout {
-  size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, idx = 0, total = 0;
+  size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, idx = 0, wot = 0, total = 0;
   int R = 1, o_stride = 0;
 };
 
-// Workspace: [status, count] header, then (prefill only) the row-chunk column flags,
-// a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and the ascending outlier column
-// list, each 256-byte aligned. A quantized-activation state (int8_quantize_activations)
-// has the same layout; neither depends on N (the GEMM epilogue dequantizes the outlier
-// columns' weights from Wq itself).
+// Quantized-activation state (int8_quantize_activations): [status, count] header, the
+// row-chunk column flags, a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and the
+// ascending outlier column list, each 256-byte aligned. The one-call workspace
+// (prefill) is the same followed by WoT, the outlier columns' weights gathered by the
+// row-quantization kernel's spare blocks; the quantize-once calls have none, and their
+// GEMM epilogue dequantizes those weights from Wq itself.
 Layout prefill_layout(int64_t M, int64_t K, int64_t max_outliers) {
   Layout L;
   size_t off = 256;
@@ -58,17 +59,19 @@ Layout prefill_layout(int64_t M, int64_t K, int64_t max_outliers) {
   L.xq = off;      off += round256(m_rows * i8mm::unit_ks(int(K)) * i8mm::kUnitK);
   L.xo = off;      off += round256(size_t(M) * L.o_stride * 2);
   L.idx = off;     off += round256(size_t(max_outliers) * 4);
-  L.total = off;
+  L.wot = L.total = off;
   return L;
 }
 
-Layout layout(int64_t M, int64_t K, int64_t max_outliers) {
+Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   if (i8mm::decode_supported(M, K)) {
     Layout L;
     L.total = 256;
     return L;
   }
-  return prefill_layout(M, K, max_outliers);
+  Layout L = prefill_layout(M, K, max_outliers);
+  L.total = L.wot + round256(size_t(N) * L.o_stride * 2);
+  return L;
 }
 
 // The weight side needs no scratch: a fixed, reserved size.
@@ -142,7 +145,7 @@ size_t int8_prepared_weight_bytes(int64_t K, int64_t N) {
 
 size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
   if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return 0;
-  return layout(M, K, max_outliers).total;
+  return layout(M, K, N, max_outliers).total;
 }
 
 int int8_mixed_matmul_is_decode(int64_t M, int64_t K) {
@@ -159,7 +162,7 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
       !aligned16(workspace) || (acc_i32 && !aligned16(acc_i32)))
     return INT8MM_E_ALIGN;
-  const Layout L = layout(M, K, max_outliers);
+  const Layout L = layout(M, K, N, max_outliers);
   if (workspace_bytes < L.total) return INT8MM_E_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
@@ -184,6 +187,7 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
   _Float16* xo = reinterpret_cast<_Float16*>(ws + L.xo);
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  _Float16* wot = reinterpret_cast<_Float16*>(ws + L.wot);
 
   if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
     return INT8MM_E_HIP;
@@ -194,12 +198,13 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   q.idx_out = max_outliers > 0 ? idx : nullptr; q.count_out = status + 1; q.status_out = status;
   q.max_outliers = int(max_outliers);
   q.Xo = xo; q.o_stride = L.o_stride;
+  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
   if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
 
   i8mm::GemmArgs g{};
   g.Wq = Wq; g.Xq = xq; g.M = int(M); g.N = int(N); g.K = int(K);
   g.a_x = a_x; g.a_w = w_absmax;
-  g.Xo = xo; g.idx = idx; g.o_stride = L.o_stride;
+  g.Xo = xo; g.WoT = wot; g.idx = idx; g.o_stride = L.o_stride;
   g.count = status + 1; g.max_outliers = int(max_outliers);
   g.Y = y; g.acc_out = acc_i32;
   if ((rc = timing_begin(stream)) != INT8MM_OK) return rc;

@@ -30,6 +30,10 @@ struct QuantRowsArgs {
   int max_outliers;
   _Float16* Xo;         // nullable: [M][o_stride] fp16 outlier activations
   int o_stride;         // multiple of 16, >= max_outliers
+  const int8_t* Wq;     // unit-tiled, for the WoT gather (nullable = no gather)
+  const float* a_w;
+  int N;
+  _Float16* WoT;        // [N][o_stride] fp16 dequantized outlier weight rows, nullable
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
 
@@ -40,6 +44,8 @@ struct GemmArgs {
   const float* a_x;
   const float* a_w;
   const _Float16* Xo;   // [M][o_stride]
+  const _Float16* WoT;  // nullable [N][o_stride]: the outlier columns' weights, gathered
+                        // beforehand; when null, the epilogue dequantizes them from Wq
   const int32_t* idx;   // ascending outlier columns, the first min(count, max_outliers) valid
   int o_stride;
   const int32_t* count;

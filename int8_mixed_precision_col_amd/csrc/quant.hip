@@ -16,6 +16,8 @@
 //                   then one wave per row: absmax over kept columns, quantize, store
 //                   Xq (row-major, or unit-tiled for the GEMM); gathers the fp16
 //                   outlier activations Xo; block 0 stores the ranked column list.
+//                   Extra blocks (one-call path) gather the dequantized int8 weight
+//                   rows of the outlier columns, WoT.
 // Both are HBM-bound streaming kernels (X read, Xq written).
 #include "common.hpp"
 #include "launch.hpp"
@@ -150,15 +152,16 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
     for (int c = nchunk + lane; c < ks * 8; c += 64) *reinterpret_cast<v2u*>(dst(c)) = v2u{0u, 0u};
 }
 
-// Block b: rows 4b..4b+3 (one wave each). Dynamic LDS: W mask words, then o_lds ranked
-// columns.
+// Blocks [0, nrow): rows 4b..4b+3 (one wave each). Blocks [nrow, nrow + ngather): WoT
+// rows n = 256 (b - nrow) + tid. Dynamic LDS: W mask words, then o_lds ranked columns.
 template <int CH>
-__global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int o_lds) {
+__global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int o_lds, int nrow) {
   extern __shared__ uint32_t lds[];
   uint32_t* words = lds;
   int* idx_s = reinterpret_cast<int*>(lds + W);
   __shared__ int wave_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool row_block = static_cast<int>(blockIdx.x) < nrow;
   const int row = blockIdx.x * 4 + wave;
 
   // 1. column mask = OR of the row-chunk flags
@@ -201,14 +204,35 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
   // outlier columns actually carried (padded to the 16-wide fp16 MFMA step)
   const int o_pad = min((count + 15) & ~15, a.o_stride);
 
-  if (row >= a.M) return;
-  const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
-  v8h v[CH > 0 ? CH : 1];
-  if constexpr (CH > 0) load_row<CH>(xr, a.K, lane, v);
-  quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane, v);
-  if (a.Xo) {
-    _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
-    for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
+  if (row_block) {
+    if (row >= a.M) return;
+    const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
+    v8h v[CH > 0 ? CH : 1];
+    if constexpr (CH > 0) load_row<CH>(xr, a.K, lane, v);
+    quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane, v);
+    if (a.Xo) {
+      _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
+      for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
+    }
+  } else {
+    // WoT[n, r] = fp16(Wq[n, O_r] * a_w[n] / 127): the outlier columns' weights,
+    // dequantized from the int8 copy that is the only weight kept in memory.
+    const int n = (blockIdx.x - nrow) * 256 + tid;
+    if (n >= a.N) return;
+    const float aw = a.a_w[n];
+    const int ks = unit_ks(a.K);
+    _Float16* dst = a.WoT + static_cast<size_t>(n) * a.o_stride;
+    for (int r0 = 0; r0 < o_pad; r0 += 8) {
+      v8h o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        o[e] = r < count ? static_cast<_Float16>(
+                               __fdiv_rn(static_cast<float>(a.Wq[unit_offset(n, idx_s[r], ks)]) * aw, 127.0f))
+                         : _Float16(0);
+      }
+      *reinterpret_cast<v8h*>(dst + r0) = o;
+    }
   }
 }
 
@@ -225,9 +249,11 @@ hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s) {
   const int W = (a.K + 31) / 32;
   const int o_lds = a.o_stride > a.max_outliers ? a.o_stride : a.max_outliers;
   const size_t lds = static_cast<size_t>(W + o_lds) * 4;
-  const dim3 grid((a.M + 3) / 4), block(256);
+  const int nrow = (a.M + 3) / 4;
+  const int ngather = a.WoT ? (a.N + 255) / 256 : 0;
+  const dim3 grid(nrow + ngather), block(256);
   const int per_lane = (a.K / 8 + 63) / 64;
-#define I8MM_QR(CHV) hipLaunchKernelGGL(k_quant_rows<CHV>, grid, block, lds, s, a, W, o_lds)
+#define I8MM_QR(CHV) hipLaunchKernelGGL(k_quant_rows<CHV>, grid, block, lds, s, a, W, o_lds, nrow)
   if (per_lane <= 1) I8MM_QR(1);
   else if (per_lane <= 2) I8MM_QR(2);
   else if (per_lane <= 4) I8MM_QR(4);

@@ -102,13 +102,13 @@ def test_workspace_sizes(L):
     assert L.int8_mixed_matmul_is_decode(8, 8192) == 1
     assert L.int8_mixed_matmul_is_decode(8, 8208) == 0
     assert L.int8_mixed_matmul_is_decode(4, 8192) == 1
-    # prefill: Xq + a_x + Xo + the outlier column list (+ flags, header, alignment);
-    # the weight side needs nothing, so N does not change it
+    # prefill: Xq + a_x + Xo + the outlier column list + the gathered outlier weight
+    # rows WoT (+ flags, header, alignment)
     M, K, N, mo = 2048, 4096, 16384, 256
     b = ws(M, K, N, mo)
-    assert b >= M * K + 4 * M + 2 * M * mo + 4 * mo
-    assert b < M * K + 4 * M + 2 * M * mo + 4 * mo + (1 << 20)
-    assert ws(M, K, N, 0) < b and ws(M + 1, K, N, mo) > b and ws(M, K, 2 * N, mo) == b
+    assert b >= M * K + 4 * M + 2 * M * mo + 4 * mo + 2 * N * mo
+    assert b < M * K + 4 * M + 2 * M * mo + 4 * mo + 2 * N * mo + (1 << 20)
+    assert ws(M, K, N, 0) < b and ws(M + 1, K, N, mo) > b and ws(M, K, N + 16, mo) > b
     assert b % 256 == 0
 
 
@@ -132,8 +132,9 @@ def test_weight_only_rejects(L):
 def test_quantize_once_rejects_and_sizes(L):
     assert L.int8_quant_state_bytes(0, 64, 16) == 0
     assert L.int8_quant_state_bytes(4096, 12288, 256) > 4096 * 12288   # holds Xq
-    assert L.int8_quant_state_bytes(2048, 4096, 256) == L.int8_mixed_matmul_workspace_bytes(
-        2048, 4096, 4096, 256)                                        # the same layout
+    # the one-call workspace is the state followed by the gathered weight rows
+    assert L.int8_quant_state_bytes(2048, 4096, 256) + 2 * 4096 * 256 == \
+        L.int8_mixed_matmul_workspace_bytes(2048, 4096, 4096, 256)
     assert L.int8_mixed_matmul_q_workspace_bytes(512, 256) == 256       # reserved, fixed
     assert L.int8_mixed_matmul_q_workspace_bytes(24, 16) == 0
     qa = L.int8_quantize_activations
