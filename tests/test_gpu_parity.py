@@ -207,7 +207,7 @@ def test_decode_every_instantiation(M, K):
     check_y(Y, ref["Y"])
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 1024, 256), (200, 1040, 528)])
+@pytest.mark.parametrize("M,K,N", [(16, 1024, 256), (200, 1040, 528), (40, 1040, 528)])
 def test_zero_outlier_invariant(M, K, N):
     """t = +inf: no outlier columns; Y is the dequantized int8 product."""
     announce(f"zero-outlier invariant M={M} K={K} N={N}")
@@ -219,7 +219,7 @@ def test_zero_outlier_invariant(M, K, N):
     check_y(Y, ref["y_int8"].astype(np.float16))
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 512, 128), (96, 528, 272)])
+@pytest.mark.parametrize("M,K,N", [(16, 512, 128), (96, 528, 272), (40, 1024, 272)])
 def test_all_outlier_invariant(M, K, N):
     """t = 0: every column is an outlier; with a lossless int8 weight, Y = fp16(X @ W)."""
     announce(f"all-outlier invariant M={M} K={K} N={N}")
@@ -232,7 +232,7 @@ def test_all_outlier_invariant(M, K, N):
     check_y(Y, textbook)
 
 
-@pytest.mark.parametrize("M,K,N", [(8, 1024, 256), (100, 1024, 256)])
+@pytest.mark.parametrize("M,K,N", [(8, 1024, 256), (100, 1024, 256), (40, 1040, 256)])
 def test_outlier_overflow_sets_status_and_nan(M, K, N):
     announce(f"outlier overflow M={M} K={K} N={N}")
     X = planted(21 + M, M, K, n_dims=5)
@@ -249,7 +249,22 @@ def test_outlier_overflow_sets_status_and_nan(M, K, N):
     assert binding.read_status(ws2) == (0, count)
 
 
-@pytest.mark.parametrize("M,K,N", [(8, 4096, 4096), (700, 2064, 1040)])
+@pytest.mark.parametrize("M,K,N", [(100, 1024, 256), (40, 1040, 256)])
+def test_quantize_once_overflow_sets_status_and_nan(M, K, N):
+    """Too many outlier columns for the state's capacity: the state's status word says
+    so and every weight's Y is NaN (tiled and weight-stream GEMMs, whose epilogues
+    dequantize the outlier weights from the column list and must not read past it)."""
+    announce(f"quantize-once overflow M={M} K={K} N={N}")
+    X = planted(41 + M, M, K, n_dims=5)
+    Wq, aw = binding.prepare_weight(dev(weight(42, K, N)))
+    qa = binding.QuantizedActivations(dev(X), 6.0, 2)
+    status, count = binding.read_status(qa.state)
+    assert status == 7 and count >= 5
+    assert torch.isnan(qa.matmul(Wq, aw)).all().item()
+    assert all(torch.isnan(y).all().item() for y in qa.matmul_grouped([(Wq, aw), (Wq, aw)]))
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 4096, 4096), (700, 2064, 1040), (40, 2064, 1040)])
 def test_deterministic(M, K, N):
     announce(f"determinism M={M} K={K} N={N}")
     X = dev(planted(31, M, K))
