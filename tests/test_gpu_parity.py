@@ -350,7 +350,8 @@ def test_weight_only_parity(M, K, N):
 
 
 @pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
-                                    (64, 8192, (256,)), (5, 1024, (32784, 65552))])
+                                    (64, 8192, (256,)), (5, 1024, (32784, 65552)),
+                                    (129, 1040, (16608,))])
 def test_quantize_once_feeds_several_weights(M, K, Ns):
     """One activation quantization, several weights: each product equals the oracle
     (acc bit-exact, Y within tolerance) and, on the multi-kernel path, the one-call
@@ -378,7 +379,7 @@ def test_quantize_once_feeds_several_weights(M, K, Ns):
 @pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
                                     (2048, 1024, (4096, 4096, 4096)),
                                     (257, 528, (16, 48, 80, 272, 528, 16, 32, 64)),
-                                    (40, 1040, (528, 65536))])
+                                    (40, 1040, (528, 65536)), (129, 1040, (8304, 8304))])
 def test_grouped_launch_equals_per_weight_calls(M, K, Ns):
     """One grouped GEMM launch over several weights: every output equals the
     one-weight int8_mixed_matmul_q call bit for bit (small- and large-tile grids, and
