@@ -123,8 +123,8 @@ size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_
  * epilogue combines both in fp32 and rounds once to fp16.
  * M <= 16 with K <= 4096, and M <= 8 with K <= 8192, run as one bandwidth-bound kernel
  * (int8_mixed_matmul_is_decode); otherwise three kernels (outlier mask, row
- * quantization + outlier gathers, MFMA GEMM). The GEMM is tiled (256 x 256 or 128 x 128
- * outputs per block) or, for a few tokens (M <= 32, or M <= 64 with N K <= 2^26; K >=
+ * quantization + outlier gathers, MFMA GEMM). The GEMM is tiled (256 x 256, 128 x 256 or
+ * 128 x 128 outputs per block, whichever is estimated fastest) or, for a few tokens (M <= 32, or M <= 64 with N K <= 2^26; K >=
  * 1024), a weight stream with one block per 16-64 output features; both compute every
  * output with the same arithmetic, so Y does not depend on which one runs.
  */
@@ -141,11 +141,12 @@ int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
  * projections fed by one X: [Abstract], the decomposition applies to the
  * feed-forward and attention projection layers). int8_quantize_activations runs
  * the outlier detection and row quantization of int8_mixed_matmul into `state`;
- * int8_mixed_matmul_q then runs the weight side (outlier weight gather, int8 MFMA
- * GEMM, fp16 outlier product, dequant epilogue) for one weight from that state.
- * Y equals int8_mixed_matmul's bit for bit when int8_mixed_matmul takes its
- * multi-kernel path (M > 16 or large K); for decode shapes the same values are
- * reached through the GEMM instead of the single decode kernel.
+ * int8_mixed_matmul_q then runs the weight side (int8 MFMA GEMM whose epilogue
+ * dequantizes the outlier columns' weights, fp16 outlier product, dequant) for one
+ * weight from that state. Y equals int8_mixed_matmul's bit for bit when
+ * int8_mixed_matmul takes its multi-kernel path (int8_mixed_matmul_is_decode(M, K) is
+ * 0); for decode shapes the same values are reached through the GEMM instead of the
+ * single decode kernel.
  *   state         device buffer of int8_quant_state_bytes(M, K, max_outliers),
  *                 written by int8_quantize_activations, read by int8_mixed_matmul_q;
  *                 it holds the status word (int8mm_read_status works on it).

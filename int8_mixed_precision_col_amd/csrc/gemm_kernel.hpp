@@ -459,7 +459,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs g, int tiles_m, int gro
 // Several weights against one quantized activation in one launch: the groups' column
 // tiles are laid side by side (group q owns virtual tile columns [tn_first[q],
 // tn_first[q + 1])), the XCD-aware order runs over that combined grid, and each block
-// multiplies with its group's weight, constants, outlier rows and output.
+// multiplies with its group's weight, constants and output (the outlier columns'
+// weights dequantized from that weight in the epilogue).
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_gemm_grouped(GroupedGemmArgs ga, int tiles_m,
                                                         int group_m) {
