@@ -36,7 +36,7 @@ MALL_BYTES = 256 << 20       # last-level cache to defeat when re-reading weight
 
 
 def log(msg: str) -> None:
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    print(f"[bench {time.time():.3f}] {msg}", file=sys.stderr, flush=True)
 
 
 def source_digest(*names: str) -> str:
