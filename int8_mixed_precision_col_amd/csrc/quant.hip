@@ -81,13 +81,14 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
 // disagrees take quant8_exact.
 // Loads a row into registers for quant_one_row<CH> (CH > 0): chunk c = lane + 64 i;
 // unconditional loads at clamped addresses, zeros past the row.
-template <int CH>
-__device__ __forceinline__ void load_row(const _Float16* __restrict__ xr, int K, int lane,
+// (STRIDE threads share the row: chunk c = t + STRIDE i.)
+template <int CH, int STRIDE = 64>
+__device__ __forceinline__ void load_row(const _Float16* __restrict__ xr, int K, int t,
                                          v8h (&v)[CH > 0 ? CH : 1]) {
   const int nchunk = K >> 3;
 #pragma unroll
   for (int i = 0; i < (CH > 0 ? CH : 1); ++i) {
-    const int c = lane + 64 * i;
+    const int c = t + STRIDE * i;
     const v8h t = *reinterpret_cast<const v8h*>(xr + min(c, nchunk - 1) * 8);
     v[i] = c < nchunk ? t : v8h{};
   }
@@ -152,17 +153,63 @@ __device__ __forceinline__ void quant_one_row(const _Float16* __restrict__ xr, i
     for (int c = nchunk + lane; c < ks * 8; c += 64) *reinterpret_cast<v2u*>(dst(c)) = v2u{0u, 0u};
 }
 
-// Blocks [0, nrow): rows 4b..4b+3 (one wave each). Blocks [nrow, nrow + ngather): WoT
-// rows n = 256 (b - nrow) + tid. Dynamic LDS: W mask words, then o_lds ranked columns.
+// One row quantized by a whole 256-thread block (for a handful of rows, where a wave
+// per row would leave the GPU idle and make each row a long serial chain): thread t
+// takes chunks t + 256 i (CH > 0, held in registers), the row constant is reduced over
+// the wave with DPP and over the 4 waves through red_s, then the same codes as
+// quant_one_row.
 template <int CH>
+__device__ __forceinline__ void quant_row_block(const _Float16* __restrict__ xr, int K,
+                                                const uint32_t* words, int8_t* __restrict__ Xq,
+                                                int row, int ks, float* a_x_row, int tid,
+                                                v8h (&v)[CH], unsigned* red_s) {
+  static_assert(CH > 0, "registers only");
+  const int nchunk = K >> 3;
+  auto dst = [&](int c) -> int8_t* {
+    return ks ? Xq + unit_offset(row, c * 8, ks) : Xq + static_cast<size_t>(row) * K + c * 8;
+  };
+  unsigned pm = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    const unsigned mb = c < nchunk ? (words[c >> 2] >> ((c & 3) << 3)) & 0xFFu : 0u;
+    if (mb) drop_halves(v[i], mb);  // outlier columns are rare
+    const v4u u = __builtin_bit_cast(v4u, v[i]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) pm = pk_max_u16(pm, u[d] & 0x7fff7fffu);
+  }
+  const unsigned wm = wave_max_u32(max(pm & 0xffffu, pm >> 16));
+  if ((tid & 63) == 0) red_s[tid >> 6] = wm;
+  lds_barrier();
+  const unsigned h = max(max(red_s[0], red_s[1]), max(red_s[2], red_s[3]));
+  const float m = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
+  const QuantBracket br = quant_bracket(m);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    unsigned dis;
+    v2u o = quant8_fast(v[i], br, dis);
+    if (dis) o = quant8_exact(v[i], m, br.lo);
+    if (c < nchunk) *reinterpret_cast<v2u*>(dst(c)) = o;
+  }
+  if (tid == 0) *a_x_row = m;
+  if (ks)
+    for (int c = nchunk + tid; c < ks * 8; c += 256) *reinterpret_cast<v2u*>(dst(c)) = v2u{0u, 0u};
+}
+
+// Blocks [0, nrow): rows 4b..4b+3 (one wave each; WIDE: row b, the whole block).
+// Blocks [nrow, nrow + ngather): WoT
+// rows n = 256 (b - nrow) + tid. Dynamic LDS: W mask words, then o_lds ranked columns.
+template <int CH, bool WIDE>
 __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int o_lds, int nrow) {
   extern __shared__ uint32_t lds[];
   uint32_t* words = lds;
   int* idx_s = reinterpret_cast<int*>(lds + W);
   __shared__ int wave_tot[4];
+  __shared__ unsigned red_s[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool row_block = static_cast<int>(blockIdx.x) < nrow;
-  const int row = blockIdx.x * 4 + wave;
+  const int row = WIDE ? static_cast<int>(blockIdx.x) : blockIdx.x * 4 + wave;
 
   // 1. column mask = OR of the row-chunk flags
   for (int w = tid; w < W; w += 256) {
@@ -205,14 +252,21 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
   const int o_pad = min((count + 15) & ~15, a.o_stride);
 
   if (row_block) {
-    if (row >= a.M) return;
+    if (row >= a.M) return;  // block-uniform when WIDE
     const _Float16* xr = a.X + static_cast<size_t>(row) * a.K;
     v8h v[CH > 0 ? CH : 1];
-    if constexpr (CH > 0) load_row<CH>(xr, a.K, lane, v);
-    quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane, v);
+    if constexpr (WIDE) {
+      load_row<CH, 256>(xr, a.K, tid, v);
+      quant_row_block<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row,
+                          tid, v, red_s);
+    } else {
+      if constexpr (CH > 0) load_row<CH>(xr, a.K, lane, v);
+      quant_one_row<CH>(xr, a.K, words, a.Xq, row, a.xq_tiled ? unit_ks(a.K) : 0, a.a_x + row, lane, v);
+    }
     if (a.Xo) {
       _Float16* xo = a.Xo + static_cast<size_t>(row) * a.o_stride;
-      for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
+      const int t0 = WIDE ? tid : lane, ts = WIDE ? 256 : 64;
+      for (int r = t0; r < o_pad; r += ts) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
     }
   } else {
     // WoT[n, r] = fp16(Wq[n, O_r] * a_w[n] / 127): the outlier columns' weights,
@@ -245,24 +299,37 @@ hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
   return hipGetLastError();
 }
 
+// A row per wave, or, below 256 rows (where M waves would leave most of the GPU idle
+// and each row one long serial chain), a row per 4-wave block.
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s) {
   const int W = (a.K + 31) / 32;
   const int o_lds = a.o_stride > a.max_outliers ? a.o_stride : a.max_outliers;
   const size_t lds = static_cast<size_t>(W + o_lds) * 4;
-  const int nrow = (a.M + 3) / 4;
+  const int nchunk = a.K / 8;
+  const bool wide = a.M < 256 && (nchunk + 255) / 256 <= 16;
+  const int nrow = wide ? a.M : (a.M + 3) / 4;
   const int ngather = a.WoT ? (a.N + 255) / 256 : 0;
   const dim3 grid(nrow + ngather), block(256);
-  const int per_lane = (a.K / 8 + 63) / 64;
-#define I8MM_QR(CHV) hipLaunchKernelGGL(k_quant_rows<CHV>, grid, block, lds, s, a, W, o_lds, nrow)
-  if (per_lane <= 1) I8MM_QR(1);
-  else if (per_lane <= 2) I8MM_QR(2);
-  else if (per_lane <= 4) I8MM_QR(4);
-  else if (per_lane <= 8) I8MM_QR(8);
-  else if (per_lane <= 16) I8MM_QR(16);
-  else if (per_lane <= 24) I8MM_QR(24);
-  else if (per_lane <= 32) I8MM_QR(32);
-  else if (per_lane <= 40) I8MM_QR(40);
-  else I8MM_QR(0);
+#define I8MM_QR(CHV, WV) hipLaunchKernelGGL((k_quant_rows<CHV, WV>), grid, block, lds, s, a, W, o_lds, nrow)
+  if (wide) {
+    const int per_thread = (nchunk + 255) / 256;
+    if (per_thread <= 1) I8MM_QR(1, true);
+    else if (per_thread <= 2) I8MM_QR(2, true);
+    else if (per_thread <= 4) I8MM_QR(4, true);
+    else if (per_thread <= 8) I8MM_QR(8, true);
+    else I8MM_QR(16, true);
+  } else {
+    const int per_lane = (nchunk + 63) / 64;
+    if (per_lane <= 1) I8MM_QR(1, false);
+    else if (per_lane <= 2) I8MM_QR(2, false);
+    else if (per_lane <= 4) I8MM_QR(4, false);
+    else if (per_lane <= 8) I8MM_QR(8, false);
+    else if (per_lane <= 16) I8MM_QR(16, false);
+    else if (per_lane <= 24) I8MM_QR(24, false);
+    else if (per_lane <= 32) I8MM_QR(32, false);
+    else if (per_lane <= 40) I8MM_QR(40, false);
+    else I8MM_QR(0, false);
+  }
 #undef I8MM_QR
   return hipGetLastError();
 }
