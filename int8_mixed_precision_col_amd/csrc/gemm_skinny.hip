@@ -70,9 +70,14 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
 
   // this wave's K steps: wave + 8 i for i < nmine. Loads are unconditional (a guarded
   // load becomes a branch whose join waits for every load in flight): slots past the
-  // wave's share read one zero line and are not multiplied.
+  // wave's share read one zero line and are not multiplied, and so do the lanes of
+  // activation rows past M (their products land in discarded outputs), which spares
+  // most of the activation reads when M is well below 16.
   const int nmine = ks > wave ? (ks - wave + kSkWaves - 1) / kSkWaves : 0;
   const int8_t* zero = reinterpret_cast<const int8_t*>(kSkZero);
+  bool tok_in[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) tok_in[q] = 16 * q + (lane & 15) < M;
   v4i acc[RG][G];
 #pragma unroll
   for (int r = 0; r < RG; ++r)
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
         w[b][r] = *reinterpret_cast<const v4i*>(in ? wrow[r] + off : zero);
 #pragma unroll
       for (int q = 0; q < G; ++q)
-        x[b][q] = *reinterpret_cast<const v4i*>(in ? xrow[q] + off : zero);
+        x[b][q] = *reinterpret_cast<const v4i*>(in && tok_in[q] ? xrow[q] + off : zero);
     }
   };
   auto mma = [&](const v4i (&w)[kSkBatch][RG], const v4i (&x)[kSkBatch][G], int i0) {
