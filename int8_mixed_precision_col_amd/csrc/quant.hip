@@ -210,12 +210,28 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a, int W, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool row_block = static_cast<int>(blockIdx.x) < nrow;
   const int row = WIDE ? static_cast<int>(blockIdx.x) : blockIdx.x * 4 + wave;
-
-  // 1. column mask = OR of the row-chunk flags
-  for (int w = tid; w < W; w += 256) {
-    uint32_t v = 0;
-    for (int rc = 0; rc < a.R; ++rc) v |= a.partial[static_cast<size_t>(rc) * W + w];
-    words[w] = v;
+  // 1. column mask = OR of the row-chunk flags. The loads of two words x 8 row chunks
+  // are issued together (chunk indices clamped to the last one: a repeat changes no
+  // OR), so that a block waits about once for them rather than once per chunk.
+  for (int w0 = tid; w0 < W; w0 += 512) {
+    const int w1 = min(w0 + 256, W - 1);  // a repeat of word W - 1 past the end
+    uint32_t v0 = 0, v1 = 0;
+    for (int rc0 = 0; rc0 < a.R; rc0 += 8) {
+      uint32_t t0[8], t1[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const size_t base = static_cast<size_t>(min(rc0 + q, a.R - 1)) * W;
+        t0[q] = a.partial[base + w0];
+        t1[q] = a.partial[base + w1];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v0 |= t0[q];
+        v1 |= t1[q];
+      }
+    }
+    words[w0] = v0;
+    if (w0 + 256 < W) words[w0 + 256] = v1;
   }
   lds_barrier();
   // 2. rank the outlier columns: thread t owns words [t*per, (t+1)*per)
