@@ -207,6 +207,29 @@ def test_decode_every_instantiation(M, K):
     check_y(Y, ref["Y"])
 
 
+@pytest.mark.parametrize("M,K,N", [(2048, 1024, 64), (600, 2000, 48)])
+def test_lone_outlier_rows_in_every_row_chunk(M, K, N):
+    """Each outlier column holds one large value in a single row (first, middle and last
+    row chunks of the outlier-mask launch: 64 chunks of 32 rows at 2048 x 1024, 19 at
+    600 x 2000): the column mask is the OR over all chunks, so a chunk left out of it
+    would quantize that column instead of carrying it in fp16, and the int32
+    accumulators would differ."""
+    announce(f"lone outlier rows M={M} K={K} N={N}")
+    rng = np.random.default_rng([M, K, 3])
+    X = (rng.standard_normal((M, K)) * 0.5).astype(np.float32)
+    lone = {0: 3, 31: 517 % K, M // 2: 700 % K, M - 33: 901 % K, M - 1: K - 1}
+    for r, c in lone.items():
+        X[r, c] = 20.0 if r % 2 else -20.0
+    X = X.astype(np.float16)
+    W = weight(M + K, K, N)
+    ws = binding.make_workspace(M, K, N, 256)
+    ref, Y, acc = _mixed(X, W, 6.0, workspace=ws)
+    assert ref["count"] == len(set(lone.values()))
+    assert binding.read_status(ws) == (0, ref["count"])
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
 @pytest.mark.parametrize("M,K,N", [(16, 1024, 256), (200, 1040, 528), (40, 1040, 528)])
 def test_zero_outlier_invariant(M, K, N):
     """t = +inf: no outlier columns; Y is the dequantized int8 product."""
