@@ -9,6 +9,7 @@ every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -75,6 +76,12 @@ def lib() -> ctypes.CDLL:
 
 def strerror(code: int) -> str:
     return lib().int8mm_strerror(code).decode()
+
+
+@functools.lru_cache(maxsize=256)
+def _prepared_bytes(K: int, N: int) -> int:
+    """Size of a prepared weight (asked of the library once per shape)."""
+    return int(lib().int8_prepared_weight_bytes(K, N))
 
 
 def _check(rc: int, where: str) -> None:
@@ -164,9 +171,9 @@ def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold
     _need(a_w, torch.float32, "a_w")
     M, K = X.shape
     N = a_w.shape[0]
-    if Wq.numel() != int(lib().int8_prepared_weight_bytes(K, N)):
+    if Wq.numel() != _prepared_bytes(K, N):
         raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
-                         f"holds {int(lib().int8_prepared_weight_bytes(K, N))}")
+                         f"holds {_prepared_bytes(K, N)}")
     if workspace is None:
         workspace = make_workspace(M, K, N, max_outliers, X.device)
     _need(workspace, torch.uint8, "workspace")
@@ -193,9 +200,9 @@ def weight_only_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor,
     _need(a_w, torch.float32, "a_w")
     M, K = X.shape
     N = a_w.shape[0]
-    if Wq.numel() != int(lib().int8_prepared_weight_bytes(K, N)):
+    if Wq.numel() != _prepared_bytes(K, N):
         raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
-                         f"holds {int(lib().int8_prepared_weight_bytes(K, N))}")
+                         f"holds {_prepared_bytes(K, N)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(out, torch.float16, "out")
@@ -227,7 +234,7 @@ class QuantizedActivations:
         _need(Wq, torch.int8, "Wq")
         _need(a_w, torch.float32, "a_w")
         N = a_w.shape[0]
-        if Wq.numel() != int(lib().int8_prepared_weight_bytes(self.K, N)):
+        if Wq.numel() != _prepared_bytes(self.K, N):
             raise ValueError("Wq does not match (K, N)")
         wb = int(lib().int8_mixed_matmul_q_workspace_bytes(N, self.max_outliers))
         if workspace is None:
@@ -254,7 +261,7 @@ class QuantizedActivations:
         for Wq, a_w in weights:
             _need(Wq, torch.int8, "Wq")
             _need(a_w, torch.float32, "a_w")
-            if Wq.numel() != int(lib().int8_prepared_weight_bytes(self.K, a_w.shape[0])):
+            if Wq.numel() != _prepared_bytes(self.K, a_w.shape[0]):
                 raise ValueError("Wq does not match (K, N)")
             Ns.append(a_w.shape[0])
         dev = weights[0][0].device

@@ -112,6 +112,13 @@ def test_workspace_sizes(L):
     assert b % 256 == 0
 
 
+def test_binding_prepared_size_matches_library(L):
+    # the binding asks the library once per shape and reuses the answer
+    for K, N in [(16, 16), (1040, 528), (12288, 49152), (1040, 528)]:
+        assert binding._prepared_bytes(K, N) == L.int8_prepared_weight_bytes(K, N)
+    assert binding._prepared_bytes(1040, 528) == 528 * 1088
+
+
 def test_timing_read_without_launches(L):
     ms, n = binding.timing_read()
     assert (ms, n) == (0.0, 0)
