@@ -193,9 +193,9 @@ int int8_mixed_matmul_q_grouped(const void* state, int64_t M, int64_t K, int64_t
  * Weight-only int8 product for a handful of tokens: Y = X · Ŵ with
  * Ŵ[k, n] = Wq[n, k] · w_absmax[n] / 127, no activation quantization and no
  * outlier decomposition ("What is 8-bit LLM quantization?", What is special about
- * LLM.int8()?: 8-bit weight storage does not make every activation or operation
- * int8; Does INT8 always improve speed?: the decoding workload gains from the
- * smaller weight stream). The comparison point for the decode path above.
+ * LLM.int8()?: int8 weights may be paired with 16-bit activations and arithmetic;
+ * Does INT8 always improve speed?: at decode time the gain is the smaller weight
+ * stream). The comparison point for the decode path above.
  *   X, M, K       fp16 activations [M, K], 1 <= M <= 16 and M K < 2^30 (X is
  *                 read through a buffer resource, whose byte offsets are 31-bit).
  *   Wq, w_absmax  unit-tiled int8 weight and fp32 [N] from int8_prepare_weight.

@@ -93,13 +93,50 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    """True for a tensor in HIP device memory (the only memory the library takes)."""
+    return t.is_cuda
+
+
 def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not _on_device(t):
         raise ValueError(f"{name} must be a HIP device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _need_shape(t: torch.Tensor, dtype: torch.dtype, shape: tuple, device, name: str) -> None:
+    """A caller-supplied buffer the kernels write in full: dtype, contiguity, exact shape
+    and device are checked before any library call, since the kernels trust them."""
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _need_matrix(X: torch.Tensor, name: str = "X") -> tuple:
+    _need(X, torch.float16, name)
+    if X.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, K], got shape {tuple(X.shape)}")
+    return tuple(X.shape)
+
+
+def _need_weight(Wq: torch.Tensor, a_w: torch.Tensor, K: int, device) -> int:
+    """(Wq, a_w) of a prepared weight for K input features; returns N."""
+    _need(Wq, torch.int8, "Wq")
+    _need(a_w, torch.float32, "a_w")
+    if a_w.dim() != 1:
+        raise ValueError(f"a_w must be 1-D [N], got shape {tuple(a_w.shape)}")
+    N = a_w.shape[0]
+    if Wq.numel() != _prepared_bytes(K, N):
+        raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
+                         f"holds {_prepared_bytes(K, N)}")
+    if Wq.device != device or a_w.device != device:
+        raise ValueError(f"Wq and a_w must be on {device}")
+    return N
 
 
 def prepare_weight(W: torch.Tensor, layout: int = 0):
@@ -108,7 +145,7 @@ def prepare_weight(W: torch.Tensor, layout: int = 0):
     Wq is the unit-tiled int8 weight the kernels read (include/int8mm.h): a tensor of
     shape (N // 16, ceil(K / 64), 16, 64); untile_weight(Wq, K) gives the [N, K] view.
     """
-    _need(W, torch.float16, "W")
+    _need_matrix(W, "W")
     K, N = (W.shape[0], W.shape[1]) if layout == 0 else (W.shape[1], W.shape[0])
     ks = (K + 63) // 64
     if N % 16:
@@ -128,8 +165,7 @@ def untile_weight(Wq: torch.Tensor, K: int) -> torch.Tensor:
 
 def quant_rows(X: torch.Tensor, threshold: float, max_outliers: int = 256) -> dict:
     """Outlier columns + row quantization of fp16 X [M, K] (see include/int8mm.h)."""
-    _need(X, torch.float16, "X")
-    M, K = X.shape
+    M, K = _need_matrix(X)
     dev = X.device
     out = {
         "Xq": torch.empty((M, K), dtype=torch.int8, device=dev),
@@ -166,24 +202,17 @@ def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold
                  max_outliers: int = 256, workspace: torch.Tensor | None = None,
                  out: torch.Tensor | None = None, acc_out: torch.Tensor | None = None):
     """Y fp16 [M, N] = the decomposed product of X [M, K] and the prepared weight (Wq, a_w)."""
-    _need(X, torch.float16, "X")
-    _need(Wq, torch.int8, "Wq")
-    _need(a_w, torch.float32, "a_w")
-    M, K = X.shape
-    N = a_w.shape[0]
-    if Wq.numel() != _prepared_bytes(K, N):
-        raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
-                         f"holds {_prepared_bytes(K, N)}")
+    M, K = _need_matrix(X)
+    N = _need_weight(Wq, a_w, K, X.device)
+    if out is not None:
+        _need_shape(out, torch.float16, (M, N), X.device, "out")
+    if acc_out is not None:
+        _need_shape(acc_out, torch.int32, (M, N), X.device, "acc_out")
     if workspace is None:
         workspace = make_workspace(M, K, N, max_outliers, X.device)
     _need(workspace, torch.uint8, "workspace")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    _need(out, torch.float16, "out")
-    if acc_out is not None:
-        _need(acc_out, torch.int32, "acc_out")
-        if tuple(acc_out.shape) != (M, N):
-            raise ValueError("acc_out must be [M, N]")
     _check(lib().int8_mixed_matmul(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
                                    float(threshold), max_outliers, out.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(),
@@ -195,17 +224,11 @@ def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold
 def weight_only_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor,
                        out: torch.Tensor | None = None) -> torch.Tensor:
     """Y fp16 [M, N] = X · (Wq · a_w / 127)ᵀ for M <= 16 (weight-only int8, no decomposition)."""
-    _need(X, torch.float16, "X")
-    _need(Wq, torch.int8, "Wq")
-    _need(a_w, torch.float32, "a_w")
-    M, K = X.shape
-    N = a_w.shape[0]
-    if Wq.numel() != _prepared_bytes(K, N):
-        raise ValueError(f"Wq holds {Wq.numel()} bytes; a prepared weight for K={K}, N={N} "
-                         f"holds {_prepared_bytes(K, N)}")
+    M, K = _need_matrix(X)
+    N = _need_weight(Wq, a_w, K, X.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    _need(out, torch.float16, "out")
+    _need_shape(out, torch.float16, (M, N), X.device, "out")
     _check(lib().int8_weight_only_matmul(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
                                          out.data_ptr(), _stream(X)), "int8_weight_only_matmul")
     return out
@@ -216,8 +239,8 @@ class QuantizedActivations:
     several int8_mixed_matmul_q calls; holds the device state buffer."""
 
     def __init__(self, X: torch.Tensor, threshold: float = 6.0, max_outliers: int = 256):
-        _need(X, torch.float16, "X")
-        self.M, self.K = X.shape
+        self.M, self.K = _need_matrix(X)
+        self.device = X.device
         self.max_outliers = max_outliers
         nbytes = int(lib().int8_quant_state_bytes(self.M, self.K, max_outliers))
         if nbytes == 0:
@@ -231,20 +254,17 @@ class QuantizedActivations:
                workspace: torch.Tensor | None = None,
                acc_out: torch.Tensor | None = None) -> torch.Tensor:
         """Y fp16 [M, N] for one prepared weight, from this quantized X."""
-        _need(Wq, torch.int8, "Wq")
-        _need(a_w, torch.float32, "a_w")
-        N = a_w.shape[0]
-        if Wq.numel() != _prepared_bytes(self.K, N):
-            raise ValueError("Wq does not match (K, N)")
+        N = _need_weight(Wq, a_w, self.K, self.device)
+        if out is not None:
+            _need_shape(out, torch.float16, (self.M, N), self.device, "out")
+        if acc_out is not None:
+            _need_shape(acc_out, torch.int32, (self.M, N), self.device, "acc_out")
         wb = int(lib().int8_mixed_matmul_q_workspace_bytes(N, self.max_outliers))
         if workspace is None:
             workspace = torch.empty((wb,), dtype=torch.uint8, device=Wq.device)
         _need(workspace, torch.uint8, "workspace")
         if out is None:
             out = torch.empty((self.M, N), dtype=torch.float16, device=Wq.device)
-        _need(out, torch.float16, "out")
-        if acc_out is not None:
-            _need(acc_out, torch.int32, "acc_out")
         _check(lib().int8_mixed_matmul_q(self.state.data_ptr(), self.M, self.K, self.max_outliers,
                                          Wq.data_ptr(), a_w.data_ptr(), N, out.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(),
@@ -257,18 +277,16 @@ class QuantizedActivations:
         """Y fp16 [M, N_q] for each (Wq, a_w) in `weights` (at most 8), from this
         quantized X, in one GEMM launch (one per weight for a few tokens)."""
         G = len(weights)
-        Ns = []
-        for Wq, a_w in weights:
-            _need(Wq, torch.int8, "Wq")
-            _need(a_w, torch.float32, "a_w")
-            if Wq.numel() != _prepared_bytes(self.K, a_w.shape[0]):
-                raise ValueError("Wq does not match (K, N)")
-            Ns.append(a_w.shape[0])
-        dev = weights[0][0].device
+        if not 1 <= G <= 8:
+            raise ValueError(f"between 1 and 8 weights, got {G}")
+        Ns = [_need_weight(Wq, a_w, self.K, self.device) for Wq, a_w in weights]
+        dev = self.device
         if outs is None:
             outs = [torch.empty((self.M, n), dtype=torch.float16, device=dev) for n in Ns]
-        for o in outs:
-            _need(o, torch.float16, "out")
+        if len(outs) != G:
+            raise ValueError(f"{G} weights but {len(outs)} outputs")
+        for q, (o, n) in enumerate(zip(outs, Ns)):
+            _need_shape(o, torch.float16, (self.M, n), dev, f"outs[{q}]")
         n_arr = (_i64 * G)(*Ns)
         wb = int(lib().int8_mixed_matmul_q_grouped_workspace_bytes(G, n_arr, self.max_outliers))
         if workspace is None:

@@ -1,10 +1,10 @@
 // Weight-only int8 decode: Y = X * dequant(Wq)^T with fp16 activations, no activation
 // quantization and no outlier decomposition.
 //
-// "What is 8-bit LLM quantization?", What is special about LLM.int8()?: 8-bit weight
-// storage does not imply that every activation or operation is INT8; and Does INT8
-// always improve speed?: for the decoding workload the gain is the smaller weight
-// stream. This is the variant that keeps only the weight in int8: the fp16 X
+// "What is 8-bit LLM quantization?", What is special about LLM.int8()? (keeping the
+// weights in 8 bits leaves the activations and the arithmetic free to stay 16-bit) and
+// Does INT8 always improve speed? (at decode time the win is reading fewer weight
+// bytes). This is the variant that keeps only the weight in int8: the fp16 X
 // multiplies the int8 weight dequantized by its column constant, Ŵ[k, n] =
 // Wq[n, k] a_w[n] / 127, with fp32 accumulation; the constant is applied once per
 // output.

@@ -8,8 +8,8 @@ X @ W (float64) on synthetic activations with outlier feature columns:
                 per-vector constants with one constant per tensor);
   group-wise    one constant per group of G consecutive K entries, for each row
                 of X and each column of W ("What is 8-bit LLM quantization?",
-                How does INT8 quantization work?: practical implementations use
-                scales for groups or vectors of weights to reduce the error);
+                How does INT8 quantization work?: finer-grained constants, per
+                group or per vector, lower the rounding error of one global one);
   vector-wise   one constant per row of X and per column of W, no decomposition
                 (the method with threshold +inf);
   decomposed    vector-wise plus the 16-bit product over the outlier columns
@@ -38,25 +38,41 @@ def _q(v: np.ndarray, a: np.ndarray) -> np.ndarray:
     return quantize(v.astype(np.float32), np.broadcast_to(a, v.shape)).astype(np.float64)
 
 
-def tensorwise(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+def tensorwise_f64(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Tensor-wise int8 product before the final rounding: one absmax constant for
+    all of X and one for all of W; the integer product is dequantized by their
+    product (a / 127 per factor), the same expression as the oracle's outer-product
+    dequantization with every row and column constant equal."""
     ax = np.float32(np.abs(X.astype(np.float64)).max())
     aw = np.float32(np.abs(W.astype(np.float64)).max())
     acc = _q(X, ax) @ _q(W, aw)
-    return (acc * float(ax) * float(aw) / (QMAX * QMAX)).astype(np.float16)
+    return acc * (np.float64(ax) * np.float64(aw)) / (QMAX * QMAX)
 
 
-def groupwise(X: np.ndarray, W: np.ndarray, group: int) -> np.ndarray:
+def tensorwise(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    return tensorwise_f64(X, W).astype(np.float16)
+
+
+def groupwise_f64(X: np.ndarray, W: np.ndarray, group: int) -> np.ndarray:
+    """Group-wise int8 product before the final rounding: K is cut into consecutive
+    groups of `group` entries (the last one possibly shorter); within a group each
+    row of X and each column of W has its own absmax constant, and the dequantized
+    group products (outer product of the group's constants) are summed."""
     M, K = X.shape
     N = W.shape[1]
     Y = np.zeros((M, N))
     for g0 in range(0, K, group):
         xs = X[:, g0:g0 + group].astype(np.float64)
         ws = W[g0:g0 + group, :].astype(np.float64)
-        ax = np.abs(xs).max(axis=1).astype(np.float32)[:, None]      # per row of X
-        aw = np.abs(ws).max(axis=0).astype(np.float32)[None, :]      # per column of W
-        acc = _q(xs, ax) @ _q(ws, aw)
-        Y += acc * ax.astype(np.float64) * aw.astype(np.float64) / (QMAX * QMAX)
-    return Y.astype(np.float16)
+        ax = np.abs(xs).max(axis=1).astype(np.float32)      # per row of X
+        aw = np.abs(ws).max(axis=0).astype(np.float32)      # per column of W
+        acc = _q(xs, ax[:, None]) @ _q(ws, aw[None, :])
+        Y += acc * np.outer(ax.astype(np.float64), aw.astype(np.float64)) / (QMAX * QMAX)
+    return Y
+
+
+def groupwise(X: np.ndarray, W: np.ndarray, group: int) -> np.ndarray:
+    return groupwise_f64(X, W, group).astype(np.float16)
 
 
 def vectorwise(X: np.ndarray, W: np.ndarray) -> np.ndarray:

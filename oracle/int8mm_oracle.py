@@ -191,8 +191,8 @@ def mixed_matmul(X: np.ndarray, Wq: np.ndarray, a_w: np.ndarray, t: float) -> di
 def weight_only_matmul(X: np.ndarray, Wq: np.ndarray, a_w: np.ndarray) -> np.ndarray:
     """Weight-only int8: Y = fp16(X @ W^) with W^[k, n] = Wq[n, k] a_w[n] / 127.
 
-    [Explainer] "What is special about LLM.int8()?": keeping the weights in 8 bit
-    does not make every activation or operation int8. Here only the weight is
+    [Explainer] "What is special about LLM.int8()?": 8-bit weights can be paired
+    with activations and arithmetic that stay in 16 bit. Here only the weight is
     quantized; the fp16 activations multiply the dequantized weight in float64 and
     the result is rounded to fp16 once. (No outlier decomposition: the same sum as
     the outlier product of ``outlier_matmul`` taken over every column.)

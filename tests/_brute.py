@@ -80,3 +80,37 @@ def weight_only_matmul(X, W):
     What = [[Fraction(q_exact(W[k][n], a_w[n])) * a_w[n] / QMAX for n in range(N)]
             for k in range(K)]
     return [[to_fp16(sum(row[k] * What[k][n] for k in range(K))) for n in range(N)] for row in X]
+
+
+def tensorwise(X, W):
+    """One absmax constant for all of X and one for all of W; exact rational result
+    and its fp16 rounding: (Yexact, Y16)."""
+    M, K, N = len(X), len(W), len(W[0])
+    X = [[Fraction(v) for v in row] for row in X]
+    W = [[Fraction(v) for v in row] for row in W]
+    ax = max(abs(v) for row in X for v in row)
+    aw = max(abs(v) for row in W for v in row)
+    Xq = [[q_exact(v, ax) for v in row] for row in X]
+    Wq = [[q_exact(v, aw) for v in row] for row in W]
+    Yex = [[Fraction(sum(Xq[i][k] * Wq[k][n] for k in range(K))) * ax * aw / (QMAX * QMAX)
+            for n in range(N)] for i in range(M)]
+    return Yex, [[to_fp16(y) for y in row] for row in Yex]
+
+
+def groupwise(X, W, group):
+    """Constants per row of X and per column of W within each group of `group`
+    consecutive K entries (the last group may be shorter); exact rational result and
+    its fp16 rounding: (Yexact, Y16)."""
+    M, K, N = len(X), len(W), len(W[0])
+    X = [[Fraction(v) for v in row] for row in X]
+    W = [[Fraction(v) for v in row] for row in W]
+    Yex = [[Fraction(0)] * N for _ in range(M)]
+    for g0 in range(0, K, group):
+        ks = range(g0, min(K, g0 + group))
+        ax = [max(abs(X[i][k]) for k in ks) for i in range(M)]
+        aw = [max(abs(W[k][n]) for k in ks) for n in range(N)]
+        for i in range(M):
+            for n in range(N):
+                acc = sum(q_exact(X[i][k], ax[i]) * q_exact(W[k][n], aw[n]) for k in ks)
+                Yex[i][n] += Fraction(acc) * ax[i] * aw[n] / (QMAX * QMAX)
+    return Yex, [[to_fp16(y) for y in row] for row in Yex]

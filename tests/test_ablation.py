@@ -38,3 +38,114 @@ def test_without_outliers_the_schemes_agree():
     r = ablation.ablation(X, W, 6.0)
     assert r["decomposed"] == r["vector-wise"]
     assert r["vector-wise"]["rms"] < 0.02
+
+
+# ----------------------------------------------------------------- exact pins
+# The schemes the decomposition is compared with are pinned on their own, so that a
+# slip in them (a group boundary off by one, an absmax over the wrong axis, a
+# transposed operand) cannot hide behind the orderings above.
+
+from fractions import Fraction  # noqa: E402
+
+from tests import _brute  # noqa: E402
+
+
+def _case(seed, M, K, N, outliers=True):
+    rng = np.random.default_rng([seed, 17])
+    X = rng.standard_normal((M, K)) * 1.5
+    if outliers:
+        X[:, rng.integers(0, K)] = rng.choice([-1, 1], size=M) * rng.uniform(15, 40, size=M)
+    W = rng.standard_normal((K, N)) * 0.03
+    return X.astype(np.float16), W.astype(np.float16)
+
+
+@pytest.mark.parametrize("seed,M,K,N", [(1, 16, 256, 64), (2, 5, 1040, 48), (3, 33, 96, 16)])
+def test_groupwise_with_one_group_is_vectorwise(seed, M, K, N):
+    """A single group spanning K (or more) is one constant per row of X and per column
+    of W: the vector-wise product, bit for bit."""
+    X, W = _case(seed, M, K, N)
+    vec = ablation.vectorwise(X, W)
+    for group in (K, K + 16, 4 * K):
+        assert np.array_equal(ablation.groupwise(X, W, group).view(np.uint16), vec.view(np.uint16))
+
+
+@pytest.mark.parametrize("seed,M,K,N", [(4, 8, 64, 32), (5, 3, 100, 16)])
+def test_groupwise_with_unit_groups_is_the_exact_product(seed, M, K, N):
+    """Groups of one entry: every value is its own absmax, so it is coded as +-127 (or
+    0) and dequantizes to itself; the result is X @ W up to the float64 sum."""
+    X, W = _case(seed, M, K, N)
+    ref = ablation.exact_product(X, W)
+    got = ablation.groupwise_f64(X, W, 1)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,M,K,N", [(6, 12, 256, 48), (7, 4, 1040, 32)])
+def test_tensorwise_is_vectorwise_when_every_constant_coincides(seed, M, K, N):
+    """Every row of X and every column of W reaching the same absmax makes the
+    per-tensor constants equal to every per-vector one: tensor-wise equals vector-wise
+    bit for bit. Lowering one row's absmax breaks the equality (control)."""
+    rng = np.random.default_rng([seed, 3])
+    X = np.clip(rng.standard_normal((M, K)), -2.5, 2.5)
+    W = np.clip(rng.standard_normal((K, N)) * 0.02, -0.05, 0.05)
+    X[np.arange(M), rng.integers(0, K, size=M)] = 3.0 * rng.choice([-1, 1], size=M)
+    W[rng.integers(0, K, size=N), np.arange(N)] = 0.0625 * rng.choice([-1, 1], size=N)
+    X, W = X.astype(np.float16), W.astype(np.float16)
+    ten, vec = ablation.tensorwise(X, W), ablation.vectorwise(X, W)
+    assert np.array_equal(ten.view(np.uint16), vec.view(np.uint16))
+    X2 = X.copy()
+    X2[0] = np.clip(X2[0], -2.0, 2.0)          # row 0's absmax now 2, the tensor's still 3
+    assert not np.array_equal(ablation.tensorwise(X2, W), ablation.vectorwise(X2, W))
+
+
+def _exact_agreement(got_f64, got16, Yex, Y16):
+    """The float64 value is the exact rational result to rounding error, and the fp16
+    outputs differ by at most one step (double rounding), mostly not at all."""
+    ex = np.array([[float(v) for v in row] for row in Yex])
+    assert np.allclose(got_f64, ex, rtol=1e-13, atol=1e-15)
+    Yb = np.array([[float(v) for v in row] for row in Y16], dtype=np.float16)
+    ulps = np.abs(got16.view(np.int16).astype(np.int32) - Yb.view(np.int16).astype(np.int32))
+    assert ulps.max() <= 1 and (ulps == 0).mean() > 0.9
+
+
+@pytest.mark.parametrize("seed,M,K,N", [(8, 3, 16, 8), (9, 4, 24, 6), (10, 2, 40, 5)])
+def test_tensorwise_matches_exact_brute_force(seed, M, K, N):
+    X, W = _case(seed, M, K, N)
+    Yex, Y16 = _brute.tensorwise(X.astype(np.float64).tolist(), W.astype(np.float64).tolist())
+    _exact_agreement(ablation.tensorwise_f64(X, W), ablation.tensorwise(X, W), Yex, Y16)
+
+
+@pytest.mark.parametrize("seed,M,K,N,group", [(11, 3, 16, 8, 4), (12, 4, 40, 6, 16),
+                                              (13, 2, 35, 5, 8), (14, 3, 24, 4, 24)])
+def test_groupwise_matches_exact_brute_force(seed, M, K, N, group):
+    """Includes a ragged last group (K = 40 in groups of 16, K = 35 in groups of 8)."""
+    X, W = _case(seed, M, K, N)
+    Yex, Y16 = _brute.groupwise(X.astype(np.float64).tolist(), W.astype(np.float64).tolist(), group)
+    _exact_agreement(ablation.groupwise_f64(X, W, group), ablation.groupwise(X, W, group), Yex, Y16)
+
+
+def _groupwise_mutant(X, W, group, kind):
+    """groupwise_f64 with one planted mistake (test-only copies; the oracle is intact)."""
+    M, K = X.shape
+    Y = np.zeros((M, W.shape[1]))
+    step = group
+    for g0 in range(0, K, step):
+        hi = g0 + group + (1 if kind == "boundary" else 0)     # groups overlap by one
+        xs = X[:, g0:hi].astype(np.float64)
+        ws = W[g0:hi, :].astype(np.float64)
+        ax = np.abs(xs).max(axis=1).astype(np.float32)
+        aw = (np.abs(ws).max(axis=1).max() * np.ones(ws.shape[1]) if kind == "axis"
+              else np.abs(ws).max(axis=0)).astype(np.float32)  # per group instead of column
+        acc = ablation._q(xs, ax[:, None]) @ ablation._q(ws, aw[None, :])
+        Y += acc * np.outer(ax.astype(np.float64), aw.astype(np.float64)) / (127 * 127)
+    return Y
+
+
+@pytest.mark.parametrize("kind", ["boundary", "axis"])
+def test_groupwise_pin_catches_planted_mistakes(kind):
+    """Control for the pin above: an off-by-one group boundary or a weight constant
+    taken over the wrong axis fails the exact comparison."""
+    X, W = _case(12, 4, 40, 6)
+    Yex, Y16 = _brute.groupwise(X.astype(np.float64).tolist(), W.astype(np.float64).tolist(), 16)
+    bad = _groupwise_mutant(X, W, 16, kind)
+    with pytest.raises(AssertionError):
+        _exact_agreement(bad, bad.astype(np.float16), Yex, Y16)

@@ -412,11 +412,16 @@ def test_grouped_launch_equals_per_weight_calls(M, K, Ns):
     announce(f"grouped launch M={M} K={K} Ns={Ns}")
     X = planted(M + K + len(Ns), M, K, n_dims=3)
     state = binding.QuantizedActivations(dev(X), 6.0, 64)
-    weights = [binding.prepare_weight(dev(weight(M + q, K, n))) for q, n in enumerate(Ns)]
+    Ws = [weight(M + q, K, n) for q, n in enumerate(Ns)]
+    weights = [binding.prepare_weight(dev(W)) for W in Ws]
     got = state.matmul_grouped(weights)
-    for (Wq, aw), Yg in zip(weights, got):
+    q_ref = oracle.quant_rows(X, 6.0)
+    for (Wq, aw), Yg, W in zip(weights, got, Ws):
         Y1 = state.matmul(Wq, aw)
         assert np.array_equal(host(Yg).view(np.uint16), host(Y1).view(np.uint16))
-    # and against the oracle for the first weight
-    Wq_ref, aw_ref = oracle.prepare_weight(weight(M, K, Ns[0]))
-    check_y(host(got[0]), oracle.mixed_matmul(X, Wq_ref, aw_ref, 6.0)["Y"])
+        # every group against the oracle, element by element
+        Wq_ref, aw_ref = oracle.prepare_weight(W)
+        assert np.array_equal(host(binding.untile_weight(Wq, K)), Wq_ref)
+        ref = oracle.mixed_matmul(X, Wq_ref, aw_ref, 6.0)
+        assert np.array_equal(ref["Xq"], q_ref["Xq"])
+        check_y(host(Yg), ref["Y"])
