@@ -60,8 +60,10 @@ typedef enum int8mm_status {
   INT8MM_E_THRESHOLD = 4, /* threshold is NaN or negative */
   INT8MM_E_WORKSPACE = 5, /* workspace smaller than int8_mixed_matmul_workspace_bytes() */
   INT8MM_E_HIP = 6,       /* a HIP runtime call or kernel launch failed */
-  INT8MM_E_TOO_MANY_OUTLIERS = 7 /* asynchronous: more outlier columns than max_outliers;
-                                    reported only through int8mm_read_status */
+  INT8MM_E_TOO_MANY_OUTLIERS = 7, /* asynchronous: more outlier columns than max_outliers;
+                                     reported only through int8mm_read_status */
+  INT8MM_E_SCRATCH = 8    /* int8_mixed_matmul_noalloc: the shape needs more workspace
+                             than INT8MM_NOALLOC_SCRATCH_BYTES */
 } int8mm_status;
 
 /*
@@ -132,6 +134,31 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
                       void* Y, void* workspace, size_t workspace_bytes, int32_t* acc_i32,
                       hipStream_t stream);
+
+/*
+ * int8_mixed_matmul without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). The call allocates nothing and frees nothing: its workspace is a
+ * fixed array of INT8MM_NOALLOC_SCRATCH_BYTES in the library's device code, one copy
+ * per GPU, held from the library's load until the process ends. Its address is
+ * looked up on the first call on each device (make that first call outside graph
+ * capture). Same kernels, same arguments and same result as int8_mixed_matmul on a
+ * workspace of its own: Y and acc_i32 equal that call's bit for bit.
+ *   Shapes whose int8_mixed_matmul_workspace_bytes(M, K, N, max_outliers) exceeds
+ *   INT8MM_NOALLOC_SCRATCH_BYTES are rejected with INT8MM_E_SCRATCH before anything
+ *   is launched (every decode shape fits; so do prefill shapes up to, for example,
+ *   M x K = 2048 x 4096 with N = 16384 and 256 outlier columns).
+ * Every call on one GPU shares that GPU's scratch and leaves its contents behind
+ * (none of it needs to start at zero): calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller. The status
+ * word lives in the scratch and is not readable; an outlier overflow still shows as
+ * NaN in Y. Other errors as for int8_mixed_matmul.
+ */
+#define INT8MM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int int8_mixed_matmul_noalloc(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                              const float* w_absmax, int64_t N, float threshold,
+                              int64_t max_outliers, void* Y, int32_t* acc_i32,
+                              hipStream_t stream);
 
 /* 1 if int8_mixed_matmul takes the single-kernel decode path for (M, K), else 0. */
 int int8_mixed_matmul_is_decode(int64_t M, int64_t K);

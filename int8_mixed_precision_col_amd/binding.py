@@ -29,6 +29,7 @@ SIGNATURES = {
     "int8_mixed_matmul_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
     "int8_mixed_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _f32, _i64, _p, _p,
                                  ctypes.c_size_t, _p, _p]),
+    "int8_mixed_matmul_noalloc": (_int, [_p, _i64, _i64, _p, _p, _i64, _f32, _i64, _p, _p, _p]),
     "int8_mixed_matmul_is_decode": (_int, [_i64, _i64]),
     "int8_weight_only_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
     "int8_quant_state_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
@@ -46,7 +47,7 @@ SIGNATURES = {
 }
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_ALIGN", 4: "E_THRESHOLD",
-          5: "E_WORKSPACE", 6: "E_HIP", 7: "E_TOO_MANY_OUTLIERS"}
+          5: "E_WORKSPACE", 6: "E_HIP", 7: "E_TOO_MANY_OUTLIERS", 8: "E_SCRATCH"}
 
 _lib = None
 
@@ -218,6 +219,28 @@ def mixed_matmul(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor, threshold
                                    workspace.data_ptr(), workspace.numel(),
                                    acc_out.data_ptr() if acc_out is not None else None,
                                    _stream(X)), "int8_mixed_matmul")
+    return out
+
+
+def mixed_matmul_noalloc(X: torch.Tensor, Wq: torch.Tensor, a_w: torch.Tensor,
+                         threshold: float = 6.0, max_outliers: int = 256,
+                         out: torch.Tensor | None = None,
+                         acc_out: torch.Tensor | None = None) -> torch.Tensor:
+    """mixed_matmul through int8_mixed_matmul_noalloc: the library's fixed per-GPU
+    scratch instead of a workspace (nothing is allocated by the call; `out` is
+    allocated here only when not given)."""
+    M, K = _need_matrix(X)
+    N = _need_weight(Wq, a_w, K, X.device)
+    if out is not None:
+        _need_shape(out, torch.float16, (M, N), X.device, "out")
+    if acc_out is not None:
+        _need_shape(acc_out, torch.int32, (M, N), X.device, "acc_out")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(lib().int8_mixed_matmul_noalloc(X.data_ptr(), M, K, Wq.data_ptr(), a_w.data_ptr(), N,
+                                           float(threshold), max_outliers, out.data_ptr(),
+                                           acc_out.data_ptr() if acc_out is not None else None,
+                                           _stream(X)), "int8_mixed_matmul_noalloc")
     return out
 
 

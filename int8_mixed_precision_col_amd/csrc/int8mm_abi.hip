@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -102,6 +103,57 @@ int timing_end(hipStream_t s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
 
+// Validation shared by int8_mixed_matmul and int8_mixed_matmul_noalloc (everything but
+// the workspace).
+int check_mixed_args(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                     const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
+                     const void* Y, const int32_t* acc_i32) {
+  if (!X || !Wq || !w_absmax || !Y) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
+      (acc_i32 && !aligned16(acc_i32)))
+    return INT8MM_E_ALIGN;
+  return INT8MM_OK;
+}
+
+// The whole decomposed product into a workspace of layout(M, K, N, max_outliers).total
+// bytes (arguments already validated).
+int run_mixed(const void* X, int64_t M, int64_t K, const int8_t* Wq, const float* w_absmax,
+              int64_t N, float threshold, int64_t max_outliers, void* Y, void* workspace,
+              int32_t* acc_i32, hipStream_t stream);
+
+constexpr size_t kNoAllocScratchBytes = INT8MM_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch size");
+
+}  // namespace
+
+// Scratch of int8_mixed_matmul_noalloc: a file-scope device array, one copy per GPU the
+// library runs on, held until the process ends. Host code never uses its name as an
+// address (on the host it is only a stand-in for the symbol): each device's address is
+// looked up once with hipGetSymbolAddress, with that device current, and kept below.
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (resolved on the first call on the device).
+int device_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return INT8MM_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return INT8MM_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return INT8MM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,15 +208,35 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,
                       void* Y, void* workspace, size_t workspace_bytes, int32_t* acc_i32,
                       hipStream_t stream) {
-  if (!X || !Wq || !w_absmax || !Y || !workspace) return INT8MM_E_NULL;
-  if (bad_m(M) || bad_k(K) || bad_n(N) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
-  if (bad_threshold(threshold)) return INT8MM_E_THRESHOLD;
-  if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_absmax) || !aligned16(Y) ||
-      !aligned16(workspace) || (acc_i32 && !aligned16(acc_i32)))
-    return INT8MM_E_ALIGN;
-  const Layout L = layout(M, K, N, max_outliers);
-  if (workspace_bytes < L.total) return INT8MM_E_WORKSPACE;
+  if (!workspace) return INT8MM_E_NULL;
+  int rc = check_mixed_args(X, M, K, Wq, w_absmax, N, threshold, max_outliers, Y, acc_i32);
+  if (rc != INT8MM_OK) return rc;
+  if (!aligned16(workspace)) return INT8MM_E_ALIGN;
+  if (workspace_bytes < layout(M, K, N, max_outliers).total) return INT8MM_E_WORKSPACE;
+  return run_mixed(X, M, K, Wq, w_absmax, N, threshold, max_outliers, Y, workspace, acc_i32,
+                   stream);
+}
 
+int int8_mixed_matmul_noalloc(const void* X, int64_t M, int64_t K, const int8_t* Wq,
+                              const float* w_absmax, int64_t N, float threshold,
+                              int64_t max_outliers, void* Y, int32_t* acc_i32,
+                              hipStream_t stream) {
+  int rc = check_mixed_args(X, M, K, Wq, w_absmax, N, threshold, max_outliers, Y, acc_i32);
+  if (rc != INT8MM_OK) return rc;
+  if (layout(M, K, N, max_outliers).total > kNoAllocScratchBytes) return INT8MM_E_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = device_scratch(&ws)) != INT8MM_OK) return rc;
+  return run_mixed(X, M, K, Wq, w_absmax, N, threshold, max_outliers, Y, ws, acc_i32, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_mixed(const void* X, int64_t M, int64_t K, const int8_t* Wq, const float* w_absmax,
+              int64_t N, float threshold, int64_t max_outliers, void* Y, void* workspace,
+              int32_t* acc_i32, hipStream_t stream) {
+  const Layout L = layout(M, K, N, max_outliers);
   char* ws = static_cast<char*>(workspace);
   int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
   const _Float16* x = static_cast<const _Float16*>(X);
@@ -211,6 +283,10 @@ int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
   if (i8mm::launch_gemm(g, stream) != hipSuccess) return INT8MM_E_HIP;
   return timing_end(stream);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers) {
   if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return 0;
@@ -361,6 +437,8 @@ const char* int8mm_strerror(int code) {
     case INT8MM_E_WORKSPACE: return "workspace smaller than int8_mixed_matmul_workspace_bytes()";
     case INT8MM_E_HIP: return "HIP runtime error or failed kernel launch";
     case INT8MM_E_TOO_MANY_OUTLIERS: return "more outlier columns than max_outliers (Y is NaN)";
+    case INT8MM_E_SCRATCH: return "shape needs more than the allocation-free call's fixed "
+                                  "scratch (INT8MM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown int8mm status code";
   }
 }

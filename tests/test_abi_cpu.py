@@ -46,9 +46,9 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_strerror_covers_codes(L):
-    texts = {c: binding.strerror(c) for c in range(0, 8)}
+    texts = {c: binding.strerror(c) for c in range(0, 9)}
     assert texts[0] == "ok"
-    assert len(set(texts.values())) == 8
+    assert len(set(texts.values())) == 9
     assert "unknown" in binding.strerror(99)
 
 
@@ -180,3 +180,36 @@ def test_grouped_rejects_and_sizes(L):
     assert g(P, 64, 250, 16, 3, ptrs, ptrs, ns, ptrs, P, wb, None) == E_SHAPE
     assert g(P, 64, 256, 16, 3, ptrs, (P_ * 3)(P, UNALIGNED, P), ns, ptrs, P, wb, None) == E_ALIGN
     assert g(P, 64, 256, 16, 3, ptrs, ptrs, ns, ptrs, P, wb - 1, None) == E_WS
+
+
+E_SCRATCH = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20   # INT8MM_NOALLOC_SCRATCH_BYTES in include/int8mm.h
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define INT8MM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_before_any_hip_call(L):
+    """Argument errors and shapes beyond the fixed scratch are returned before the
+    library touches the device (no GPU here: any HIP call would fail differently)."""
+    na = L.int8_mixed_matmul_noalloc
+    ws = L.int8_mixed_matmul_workspace_bytes
+    assert na(None, 64, 256, P, P, 256, 6.0, 16, P, None, None) == E_NULL
+    assert na(P, 64, 256, P, P, 256, 6.0, 16, None, None, None) == E_NULL
+    assert na(P, 64, 250, P, P, 256, 6.0, 16, P, None, None) == E_SHAPE
+    assert na(P, 64, 256, P, P, 256, math.nan, 16, P, None, None) == E_THR
+    assert na(P, 64, 256, P, P, 256, 6.0, 16, P, UNALIGNED, None) == E_ALIGN
+    # a shape just over the scratch, and the 13B-like and 175B-like prefill shapes
+    M, K, N = 4096, 12288, 49152
+    assert ws(M, K, N, 256) > NOALLOC_SCRATCH_BYTES
+    assert na(P, M, K, P, P, N, 6.0, 256, P, None, None) == E_SCRATCH
+    assert ws(4096, 20480, 5120, 256) > NOALLOC_SCRATCH_BYTES
+    assert na(P, 4096, 20480, P, P, 5120, 6.0, 256, P, None, None) == E_SCRATCH
+    over = next(m for m in range(2048, 1 << 16, 256) if ws(m, 8192, 4096, 256) > NOALLOC_SCRATCH_BYTES)
+    assert na(P, over, 8192, P, P, 4096, 6.0, 256, P, None, None) == E_SCRATCH
+    # what the limit admits: every decode shape and the 6.7B-like FFN shape
+    assert ws(8, 4096, 4096, 256) <= NOALLOC_SCRATCH_BYTES
+    assert ws(2048, 4096, 16384, 256) <= NOALLOC_SCRATCH_BYTES

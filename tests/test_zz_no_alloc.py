@@ -1,0 +1,66 @@
+"""The allocation-free entry point (int8_mixed_matmul_noalloc) against the one that
+takes a workspace (int8_mixed_matmul) and the oracle: two calls in a row on the
+library's fixed scratch, the second on a smaller input, each bit-identical to the
+workspace call (same kernels) and within the oracle's tolerance; a shape beyond
+the scratch is refused before anything runs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_mixed_precision_col_amd import binding, inputs
+from tests.gpu_util import announce, check_y, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, M, K, N):
+    wl = inputs.Workload(f"na{seed}", M, K, N, 3, 15.0, 60.0, 0.75, 0.02, seed=seed)
+    X, _ = inputs.make_x(wl)
+    return X, inputs.make_w(wl)
+
+
+def _both(X, W, t=6.0, mo=256):
+    M, N = X.shape[0], W.shape[1]
+    Xd = dev(X)
+    Wq, aw = binding.prepare_weight(dev(W))
+    acc_n = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    acc_w = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y_n = binding.mixed_matmul_noalloc(Xd, Wq, aw, t, mo, acc_out=acc_n)
+    y_w = binding.mixed_matmul(Xd, Wq, aw, t, mo, acc_out=acc_w)
+    return host(y_n), host(acc_n), host(y_w), host(acc_w)
+
+
+@pytest.mark.parametrize("first,second", [
+    ((300, 1040, 528), (40, 1040, 272)),        # prefill, then a smaller prefill
+    ((2048, 4096, 16384), (8, 4096, 4096)),     # the largest workload it admits, then decode
+    ((16, 4096, 1024), (3, 2048, 512)),         # decode, then a smaller decode
+])
+def test_noalloc_two_calls_match_workspace_call_and_oracle(first, second):
+    for i, (M, K, N) in enumerate((first, second)):
+        announce(f"noalloc call {i}: M={M} K={K} N={N} "
+                 f"({'decode' if binding.is_decode(M, K) else 'prefill'})")
+        X, W = _case(M + K + N, M, K, N)
+        y_n, acc_n, y_w, acc_w = _both(X, W)
+        assert np.array_equal(acc_n, acc_w)
+        assert np.array_equal(y_n.view(np.uint16), y_w.view(np.uint16))
+        rows = np.arange(M) if M <= 64 else np.sort(np.random.default_rng(1).choice(M, 48, replace=False))
+        Wq_ref, aw_ref = oracle.prepare_weight(W)
+        q_ref = oracle.quant_rows(X, 6.0)
+        acc_ref = oracle.int8_matmul(q_ref["Xq"][rows], Wq_ref)
+        y_ref = (oracle.dequant_outer(acc_ref, q_ref["a_x"][rows], aw_ref)
+                 + oracle.outlier_matmul(X[rows], q_ref["idx"], Wq_ref, aw_ref)).astype(np.float16)
+        assert np.array_equal(acc_n[rows], acc_ref)
+        check_y(y_n[rows], y_ref)
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    announce("noalloc refuses a shape beyond the scratch")
+    M, K, N = 8192, 8192, 256
+    assert binding.workspace_bytes(M, K, N, 256) > 64 << 20
+    X = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    Wq, aw = binding.prepare_weight(torch.zeros((K, N), dtype=torch.float16, device="cuda"))
+    with pytest.raises(binding.Int8mmError) as e:
+        binding.mixed_matmul_noalloc(X, Wq, aw, 6.0, 256)
+    assert e.value.code == 8
