@@ -13,17 +13,17 @@
 //     every row of its chunks), the rows' partial absmax over the kept columns (DPP
 //     over the wave) and its outlier columns in ascending order. The eight compute
 //     waves meet through an LDS counter (the stream waves take no part); then each
-//     has the row constants, the outlier count and ranks, stages the fp16 values of
+//     has the row constants, the outlier count and ranks; it loads the weight bytes of
 //     its first outlier columns, quantizes its columns into its own LDS rows (an exact
-//     pass for the rare values the bracketing pair cannot decide) and flags them ready;
+//     pass for the rare values the bracketing pair cannot decide), flags them ready and
+//     stages the outlier columns' X and dequantized weights for the epilogue;
 //   * stream wave p issues the pair's Wq units (one 1 KB unit per load instruction,
 //     straight into registers). A wave that issues this many loads stalls in issue
 //     until the memory system accepts them; keeping the stream in waves of its own
 //     keeps those stalls away from the activation work. When its compute wave's codes
 //     are ready it runs v_mfma_i32_16x16x64_i8 over the pair's steps (Wq unit as the
-//     16-row operand, the codes of up to 16 tokens as the other), stores its int32
-//     partials and stages the dequantized weights of the pair's first outlier columns
-//     from its registers;
+//     16-row operand, the codes of up to 16 tokens as the other) and stores its int32
+//     partials;
 //   * after one block barrier, the epilogue sums the eight int32 partials exactly,
 //     applies the outer-product dequantization and adds the outlier columns' product,
 //     fp16 X times the fp16-rounded dequantized weight fp16(q a_w / 127) summed in fp32
@@ -40,7 +40,8 @@ namespace i8mm {
 constexpr int kDecMaxM = 16, kDecMaxK = 8192;
 constexpr int kDecPairs = 8;                      // compute waves = stream waves
 constexpr int kDecThreads = 2 * 64 * kDecPairs;   // 1024
-constexpr int kPre = 32;  // outlier columns staged from registers (more: loaded in passes)
+constexpr int kPre = 16;    // outlier columns staged while the codes are made
+constexpr int kChunkO = 32; // outlier columns per later epilogue pass
 #ifndef I8MM_DEC_EARLY
 #define I8MM_DEC_EARLY 2
 #endif
@@ -69,12 +70,12 @@ bool decode_supported(int64_t M, int64_t K) {
   return rows_held(M) * (K > 4096 ? 2 : 1) <= 16;
 }
 
-// Dynamic LDS: each pair's code rows [M][64 SPW + 16], the outlier column lists (one
-// segment of 64 SPW shorts per pair), and a sink of 8 bytes per lane for the code stores
-// of lanes that own no chunk.
+// Dynamic LDS: each pair's code rows [rows_held(M)][64 SPW + 16] (rows from M on are
+// scratch), the outlier column lists (one segment of 64 SPW shorts per pair), and a sink of
+// 8 bytes per lane for the code stores of lanes that own no chunk.
 static size_t decode_lds_bytes(int64_t M, int64_t K) {
   const size_t spw = static_cast<size_t>(steps_per_wave(K));
-  return kDecPairs * static_cast<size_t>(M) * (64 * spw + 16) + kDecPairs * 64 * spw * 2 + 64 * 8;
+  return kDecPairs * static_cast<size_t>(rows_held(M)) * (64 * spw + 16) + kDecPairs * 64 * spw * 2 + 64 * 8;
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   __shared__ unsigned rmax_s[kDecPairs][16];
   __shared__ int cnt_s[kDecPairs];
   __shared__ float rowmax_s[16];
-  __shared__ float xo_s[kPre * 16], wo_s[kPre * 16];
+  __shared__ float xo_s[kChunkO * 16], wo_s[kChunkO * 16];
   // [0]: compute waves past their row maxima; [1 + p]: pair p's codes ready; [9]: a
   // wait expired; [10 + p]: pair p's X has arrived
   __shared__ int sync_s[2 * kDecPairs + 2];
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = wave & (kDecPairs - 1);
   const int n0 = blockIdx.x * 16;
-  int8_t* xq_p = reinterpret_cast<int8_t*>(lds) + p * M * XS;  // pair p's codes [M][XS]
-  short* list_s = reinterpret_cast<short*>(lds + kDecPairs * M * XS);
+  int8_t* xq_p = reinterpret_cast<int8_t*>(lds) + p * MR * XS;  // pair p's codes [MR][XS]
+  short* list_s = reinterpret_cast<short*>(lds + kDecPairs * MR * XS);
   int8_t* sink = reinterpret_cast<int8_t*>(list_s + kDecPairs * WCOLS) + lane * 8;
   float aw_c = 0.0f;  // the epilogue's column constant (compute waves)
 
@@ -306,8 +307,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kDecPairs; ++w) first += w < p ? cnt_s[w] : 0;
 
-    // 6. the fp16 values of this pair's outlier columns of global rank < kPre, for the
-    // epilogue (rare: a divergent loop over the lanes holding one)
+    // 6. the pair's outlier columns of global rank < kPre, for the epilogue: their fp16 X
+    // values from the registers (a divergent loop over the lanes holding one), and their
+    // weight bytes, loaded now (lane: rank first + 4 i + l / 16, feature l % 16) so that
+    // the latency hides under the codes
 #pragma unroll
     for (int j = 0; j < CC; ++j) {
       int r = first + rfirst[j];
@@ -318,16 +321,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
           if (m < M) xo_s[r * 16 + m] = half_bits_to_float(half_at(xv[m][j], e));
       }
     }
+    const int nstage = max(0, min(wcount, kPre - first));  // wave-uniform
+    constexpr int kStageLoads = kPre / 4;  // 4 columns per load (16 lanes each)
+    int qv[kStageLoads];
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i) {
+      const int k = 4 * i + (lane >> 4);
+      const int col = k < nstage ? list_p[k] : 0;
+      qv[i] = a.Wq[unit_offset(n0 + (lane & 15), col, ks)];
+    }
 
     // 7. codes of this pair's columns into its LDS rows, outlier columns cleared (their
-    // codes are 0). The bracketing pair decides; (row, chunk) slots where it disagrees
-    // are rewritten with quant8_exact below.
-    // Rows past M hold copies of row M - 1 and store the same codes into its row (no
-    // branch per row: the rows' independent work interleaves).
-    unsigned pend = 0;
+    // codes are 0). Rows past M hold copies of row M - 1 and fill the scratch rows. The
+    // bracketing pair decides; (row, chunk) slots where it disagrees in some lane are
+    // redone with quant8_exact below.
+    unsigned long long dm[MR][CC];  // lanes where the pair disagreed
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const int mrow = min(m, M - 1);
       const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
       const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.hi), m));
 #pragma unroll
@@ -339,25 +349,31 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
         xv[m][j] = __builtin_bit_cast(v8h, u);
         bool dis;
         const v2u o = quant8_pair(xv[m][j], lo, hi, dis);
-        pend |= dis ? 1u << (m * CC + j) : 0u;
-        *reinterpret_cast<v2u*>(lc < WCH ? xq_p + mrow * XS + lc * 8 : sink) = o;
+        dm[m][j] = __ballot(dis);
+        *reinterpret_cast<v2u*>(lc < WCH ? xq_p + m * XS + lc * 8 : sink) = o;
       }
     }
-    // 8. exact codes where the pair disagreed (values at or within about 2^-15 of a
-    // half-integer, exact ties included): a wave-uniform branch, rarely taken
-    if (__ballot(pend != 0u) != 0) {
+    // 8. exact codes (values at or within about 2^-15 of a half-integer, exact ties
+    // included, make the pair disagree): wave-uniform branches, rarely taken
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const int mrow = min(m, M - 1);
-        const float am = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, am_l), m));
-        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int j = 0; j < CC; ++j) {
+      for (int j = 0; j < CC; ++j)
+        if (dm[m][j] != 0) {
+          const float am = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, am_l), m));
+          const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
           const int lc = lane + 64 * j;
-          if (pend & (1u << (m * CC + j)))
-            *reinterpret_cast<v2u*>(lc < WCH ? xq_p + mrow * XS + lc * 8 : sink) = quant8_exact(xv[m][j], am, lo);
+          if ((dm[m][j] >> lane) & 1u)
+            *reinterpret_cast<v2u*>(lc < WCH ? xq_p + m * XS + lc * 8 : sink) = quant8_exact(xv[m][j], am, lo);
         }
-      }
+    // the staged weights: W^ = fp16(q a_w / 127), the int8 weight dequantized as the GEMM
+    // epilogue forms it
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i) {
+      const int k = 4 * i + (lane >> 4);
+      if (k < nstage)
+        wo_s[(first + k) * 16 + (lane & 15)] =
+            static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv[i]) * aw_c, 127.0f)));
     }
     if (lane == 0)
       __hip_atomic_fetch_add(&sync_s[1 + p], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -376,7 +392,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < E; ++i)
       wf[i] = *reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes);
-    const float aw_s = a.a_w[n0 + (lane & 15)];
     if (!lds_wait_geq(&sync_s[2 + kDecPairs + p], 1)) sync_s[kDecPairs + 1] = 1;
 #pragma unroll
     for (int i = E; i < SPW; ++i)
@@ -397,33 +412,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     // 16x16 accumulator layout: lane l, register r -> token l % 16, feature 4 (l / 16) + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[p][4 * kg + r][tok] = acc[r];
-
-    // 10. W^ = fp16(q a_w / 127) of this pair's outlier columns of global rank < kPre (the
-    // int8 weight dequantized, as the GEMM epilogue forms it), from the registers: column
-    // c is byte c % 16 of unit step c / 64, in the lanes l with l / 16 = (c % 64) / 16
-    int first = 0;
-#pragma unroll
-    for (int w = 0; w < kDecPairs; ++w) first += w < p ? cnt_s[w] : 0;
-    const int nloc = min(cnt_s[p], kPre - first);
-    for (int k = 0; k < nloc; ++k) {  // wave-uniform
-      const int col = list_s[p * WCOLS + k];
-      const int i = (col >> 6) - SPW * p, b = col & 15;
-      v4i w = wf[0];
-#pragma unroll
-      for (int ii = 1; ii < SPW; ++ii) w = ii == i ? wf[ii] : w;
-      const int d = b >> 2;
-      const int dw = d == 0 ? w[0] : d == 1 ? w[1] : d == 2 ? w[2] : w[3];
-      const int q = static_cast<int>(static_cast<signed char>(dw >> (8 * (b & 3))));
-      if ((lane >> 4) == ((col & 63) >> 4))
-        wo_s[(first + k) * 16 + (lane & 15)] = static_cast<float>(
-            static_cast<_Float16>(__fdiv_rn(static_cast<float>(q) * aw_s, 127.0f)));
-    }
   }
   lds_barrier();
 
   // 11. epilogue: thread t < 256 -> (token m, output feature n0 + nl). The int32 partials
   // of the pairs are summed exactly; the outlier product in fp32, ascending columns, the
-  // first kPre from the staged values, the rest kPre at a time from global memory.
+  // first kPre from the staged values, the rest kChunkO at a time from global memory.
   int wb[kDecPairs + 1];
   wb[0] = 0;
 #pragma unroll
@@ -434,10 +428,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   float yo = 0.0f;
   if (tid < 256)
     for (int r = 0; r < npre; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
-  for (int r0 = kPre; r0 < count; r0 += kPre) {  // block-uniform trip count
+  for (int r0 = kPre; r0 < count; r0 += kChunkO) {  // block-uniform trip count
     lds_barrier();  // the staged values above are read
-    const int rn = min(kPre, count - r0);
-    if (tid < kPre * 16) {
+    const int rn = min(kChunkO, count - r0);
+    if (tid < kChunkO * 16) {
       const int pr = tid >> 4, pq = tid & 15;
       int col = 0;
       if (pr < rn) {
