@@ -8,10 +8,14 @@ over the workload's synthetic inputs, which are resident in HBM; the weight is
 converted to int8 once beforehand, as at checkpoint load. Prints ONE JSON line:
 `value` is the prefill effective TOPS (2 M K N / time per call). The `roofline`
 object is the GEMM kernel's own rate from HIP events recorded around its
-launches during the timed steps. The decode shape (8 tokens) is measured in
-the same run as `decode` (GB/s of algorithmic bytes; 32 calls over 32 rotated
-weights captured in one HIP graph, per-call time from events around the replays).
-`cpu_baseline` times the CPU oracle on a bounded row x column sample.
+launches during the timed steps; `kernels` splits a step into its kernels (a
+separate pass with every kernel bracketed by events). The decode shape (8 tokens)
+is measured in the same run as `decode` (GB/s of algorithmic bytes; 32 calls over
+32 rotated weights captured in one HIP graph, per-call time from events around the
+replays), next to a plain copy kernel of the same size. `configs` measures the
+other workloads (16 x 1024 x 1024, the 6.7B-like and 13B-like FFN shapes) the same
+way as the headline, and `vendor_int8_gemm` the vendor int8 GEMM on the headline
+shape. `cpu_baseline` times the CPU oracle on a bounded row x column sample.
 """
 
 from __future__ import annotations
@@ -178,9 +182,13 @@ def prepare(binding, torch, wl, inputs, copies: int, time_prepare: bool = False)
     return X, W, Xd, weights, prep
 
 
-def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y):
-    binding.timing_read()
-    binding.timing_enable(True)
+def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y, mode: int = 1):
+    """n_calls int8_mixed_matmul calls over the rotated weights, bracketed by device
+    synchronisations. mode 1: the library's events bracket each call's main kernel; mode 2:
+    also the outlier-mask and row-quantization kernels. Returns (wall ms, {phase: (ms,
+    launches)})."""
+    binding.timing_read_phases()
+    binding.timing_enable(mode)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n_calls):
@@ -188,9 +196,20 @@ def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y):
         binding.mixed_matmul(Xd, Wq, aw, wl.threshold, MAX_OUTLIERS, workspace=ws, out=Y)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    binding.timing_enable(False)
-    kern_ms, launches = binding.timing_read()
-    return (t1 - t0) * 1e3, kern_ms, launches
+    binding.timing_enable(0)
+    return (t1 - t0) * 1e3, binding.timing_read_phases()
+
+
+def phase_breakdown(phases: dict, n_calls: int, wall_ms: float) -> dict:
+    """Per-kernel time per call (us) and its share of the call, from a mode-2 timing pass
+    (every kernel bracketed by events) whose own wall time is wall_ms."""
+    out = {"pass_ms_per_call": wall_ms / n_calls}
+    for name, (ms, n) in phases.items():
+        if n:
+            us = ms / n_calls * 1e3
+            out[name] = {"us_per_call": us, "launches_per_call": n / n_calls,
+                         "share_of_call": ms / wall_ms}
+    return out
 
 
 def cpu_baseline(oracle, X, W, wl, budget_s: float = 15.0) -> dict:
@@ -222,11 +241,113 @@ def cpu_baseline(oracle, X, W, wl, budget_s: float = 15.0) -> dict:
     ops = 2.0 * ms * wl.K * ns
     threads = [d.get("num_threads", 1) for d in threadpool_info()
                if d.get("internal_api") in ("openblas", "mkl", "blis")]
-    cores = max(threads) if threads else 1
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+    blas = max(threads) if threads else 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": cores, "blas_threads": blas,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"all {ms} rows x output columns 0..{ns - 1} of {wl.name} "
                       f"(M={ms}, K={wl.K}, N={ns}), {t:.1f} s for one oracle call "
-                      f"(numpy float64 BLAS on {cores} threads)"}
+                      f"(numpy float64; the BLAS product on {blas} threads, the elementwise "
+                      f"steps on one; {cores} cores in the process's affinity set)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_config(binding, torch, inputs, name: str, calls: int = 20, warmup: int = 3) -> dict:
+    """One workload end to end: wall time per int8_mixed_matmul call over weights rotated to
+    defeat the last-level cache (hook off), then a pass with every kernel of the call
+    bracketed by events for the per-kernel breakdown."""
+    wl = inputs.WORKLOADS[name]
+    copies = max(1, -(-MALL_BYTES // (wl.N * wl.K)))
+    _, _, Xd, weights, _ = prepare(binding, torch, wl, inputs, copies)
+    ws = binding.make_workspace(wl.M, wl.K, wl.N, MAX_OUTLIERS)
+    Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+    time_calls(binding, torch, Xd, weights, wl, warmup, ws, Y, mode=0)
+    wall_ms, _ = time_calls(binding, torch, Xd, weights, wl, calls, ws, Y, mode=0)
+    ms = wall_ms / calls
+    wall2, phases = time_calls(binding, torch, Xd, weights, wl, calls, ws, Y, mode=2)
+    status, count = binding.read_status(ws)
+    assert status == 0 and torch.isfinite(Y).all().item(), f"{name}: bad result (status {status})"
+    decode = binding.is_decode(wl.M, wl.K)
+    main_ms, main_n = phases["main"]
+    main_ms /= max(main_n, 1)
+    ops = float(wl.flops)
+    res = {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "outlier_cols": count,
+           "path": "decode kernel" if decode else "outlier mask + row quantization + GEMM",
+           "weights_rotated": copies, "calls": calls,
+           "ms_per_call": ms, "TOPS": ops / (ms * 1e-3) / 1e12,
+           "kernels": phase_breakdown(phases, calls, wall2),
+           "main_kernel": {"ms": main_ms, "TOPS": ops / (main_ms * 1e-3) / 1e12,
+                           "frac_of_int8_peak": ops / (main_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}}
+    if decode:
+        alg = wl.M * wl.K * 2 + wl.N * wl.K + wl.N * 4 + wl.M * wl.N * 2
+        res["main_kernel"]["GB/s"] = alg / (main_ms * 1e-3) / 1e9
+        res["main_kernel"]["frac_of_hbm_peak"] = res["main_kernel"]["GB/s"] / PEAK_HBM_GBS
+    del Xd, weights, ws, Y
+    torch.cuda.empty_cache()
+    return res
+
+
+def measured_copy_floor(torch, nbytes: int = 8 << 20, copies: int = 32, reps: int = 20) -> dict:
+    """A plain elementwise kernel (bitwise NOT of uint8: reads and writes nbytes, 16 MiB
+    moved in all, about what one decode call reads) over rotated buffers, captured like the
+    decode calls: what one launch moving that much achieves on this GPU, for comparison
+    with the decode kernel."""
+    src = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for s in src[:2]:
+        torch.bitwise_not(s, out=dst)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in src:
+            torch.bitwise_not(s, out=dst)
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * copies) * 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "torch bitwise_not (uint8)", "bytes_read": nbytes, "bytes_written": nbytes,
+            "us_per_call": us, "GB/s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
+def vendor_int8_gemm(torch, M: int, K: int, N: int, reps: int = 5) -> dict | None:
+    """The vendor int8 GEMM (torch._int_mm, int32 output) on the same shape, without any
+    of the decomposition: a measured reference for the MFMA GEMM."""
+    try:
+        A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        B = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda").t()
+        torch._int_mm(A, B)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch._int_mm(A, B)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del A, B
+        torch.cuda.empty_cache()
+        return {"op": "torch._int_mm (int8 x int8 -> int32)", "ms": ms,
+                "TOPS": 2.0 * M * K * N / (ms * 1e-3) / 1e12}
+    except (RuntimeError, AttributeError) as e:  # not every build has a kernel for it
+        return {"op": "torch._int_mm", "error": str(e)[:200]}
 
 
 def bench_projections(binding, torch, inputs, reps: int = 10) -> dict:
@@ -287,9 +408,9 @@ def bench_decode(binding, torch, inputs, reps: int) -> dict:
     Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
     # eager: per-launch kernel time from the library's event hook, for context
     time_calls(binding, torch, Xd, weights, wl, copies * 2, ws, Y)
-    wall_ms, kern_ms, launches = time_calls(binding, torch, Xd, weights, wl, copies * 4, ws, Y)
+    wall_ms, phases = time_calls(binding, torch, Xd, weights, wl, copies * 4, ws, Y)
     eager_us = wall_ms / (copies * 4) * 1e3
-    hook_us = kern_ms / launches * 1e3
+    hook_us = phases["main"][0] / phases["main"][1] * 1e3
     status, count = binding.read_status(ws)
     assert status == 0, f"decode status {status}"
     Y_ref = binding.mixed_matmul(Xd, *weights[-1], wl.threshold, MAX_OUTLIERS, workspace=ws).clone()
@@ -351,7 +472,11 @@ def bench_decode(binding, torch, inputs, reps: int) -> dict:
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
                      "traffic": load_traffic("k_decode", wl.name),
-                     "kernel": "k_decode", "kernel_avg_us": per_call_us},
+                     "kernel": "k_decode",
+                     "time_basis": "per call of a captured graph of 32 calls (the gap between "
+                                   "launches included)",
+                     "per_call_us": per_call_us,
+                     "measured_floor": measured_copy_floor(torch)},
     }
 
 
@@ -363,6 +488,8 @@ def main() -> int:
     ap.add_argument("--workload", default="175b_layer_share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny / 6.7B / 13B workloads and the vendor GEMM reference")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the copy probe, then the steps, and print no JSON (for --pmc runs)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -398,7 +525,8 @@ def main() -> int:
     log(f"warmup {args.warmup}")
     time_calls(binding, torch, Xd, weights, wl, args.warmup, ws, Y)
     log(f"timing {args.steps} steps")
-    wall_ms, kern_ms, launches = time_calls(binding, torch, Xd, weights, wl, args.steps, ws, Y)
+    wall_ms, phases = time_calls(binding, torch, Xd, weights, wl, args.steps, ws, Y)
+    kern_ms, launches = phases["main"]
     status, count = binding.read_status(ws)
     if status != 0 or not torch.isfinite(Y).all().item():
         raise SystemExit(f"bad result: status {status}")
@@ -426,6 +554,10 @@ def main() -> int:
                      "traffic": load_traffic("k_gemm", wl.name),
                      "kernel": "k_gemm", "kernel_avg_ms": gemm_avg_ms},
     }
+    # per-kernel breakdown of the step, in a pass of its own (every kernel bracketed)
+    n2 = max(3, args.steps // 4)
+    wall2, ph2 = time_calls(binding, torch, Xd, weights, wl, n2, ws, Y, mode=2)
+    result["kernels"] = phase_breakdown(ph2, n2, wall2)
     result["prepare_weight"] = prep
     # the GPU path and the CPU baseline below read these same host arrays
     result["inputs_sha256_16"] = {"X_fp16": array_digest(X), "W_fp16": array_digest(W)}
@@ -440,6 +572,13 @@ def main() -> int:
     if not args.no_decode:
         log("projections sharing one input")
         result["projections_qkv"] = bench_projections(binding, torch, inputs)
+    if not args.no_configs:
+        result["configs"] = {}
+        for name in ("tiny", "opt6.7b_ffn_up", "13b_ffn_down"):
+            log(f"config {name}")
+            result["configs"][name] = bench_config(binding, torch, inputs, name)
+        log("vendor int8 GEMM on the headline shape")
+        result["vendor_int8_gemm"] = vendor_int8_gemm(torch, wl.M, wl.K, wl.N)
     if not args.no_cpu_baseline:
         import oracle
 

@@ -80,6 +80,21 @@ int int8_prepare_weight(const void* W, int64_t K, int64_t N, int w_layout, int8_
                         float* w_absmax, hipStream_t stream);
 
 /*
+ * An int8 weight that is already quantized ([Abstract]: a checkpoint converted to Int8
+ * is used as it is loaded; one fp32 constant per output column), handed over as the
+ * plain [N, K] matrix: copies it into the unit-tiled layout the matmul calls read.
+ * Layout only, no arithmetic: the caller's constants w_absmax [N] are used unchanged
+ * with the result (the codes must be those of q(W, w_absmax), in [-127, 127], for the
+ * product to be the method's). The unit-tiled layout is what every matmul call takes
+ * in place of a plain [N, K] Wq.
+ *   Wq_nk     int8 [N, K] row-major (K contiguous).
+ *   Wq        out, int8_prepared_weight_bytes(K, N) bytes, unit-tiled; the K padding of
+ *             each row's last unit is zero.
+ * Errors: NULL pointers, K or N outside the limits above, pointers not 16-byte aligned.
+ */
+int int8_tile_weight(const int8_t* Wq_nk, int64_t K, int64_t N, int8_t* Wq, hipStream_t stream);
+
+/*
  * Outlier detection plus vector-wise row quantization of the activations
  * ([Blog] "Vector-wise quantization": one constant per input row;
  * [Abstract]/[Summary]: outlier feature dimensions are isolated).
@@ -247,14 +262,18 @@ int int8mm_read_status(const void* workspace, int32_t* n_outliers, hipStream_t s
 const char* int8mm_strerror(int code);
 
 /*
- * Optional timing of the main kernel (the MFMA GEMM, or the decode kernel):
- * while enabled, each int8_mixed_matmul call records a HIP event pair around
- * that launch on its stream. int8mm_timing_read synchronises on the recorded
- * events, returns the summed milliseconds and launch count since the last
- * read, and starts a new period. Not thread-safe.
+ * Optional event timing, for benchmarks. int8mm_timing_enable(mode): 0 off; 1: each call
+ * records a HIP event pair on its stream around its main kernel (the MFMA GEMM, the
+ * decode kernel or the weight-only kernel); 2: also around the outlier-mask and
+ * row-quantization kernels. Other modes are INT8MM_E_SHAPE. Not for calls under graph
+ * capture (the events would be captured). int8mm_timing_read_phases synchronises on the
+ * recorded events and returns, per phase (0 outlier mask, 1 row quantization, 2 main
+ * kernel), the summed milliseconds and launch counts since the last read, then starts a
+ * new period; int8mm_timing_read does the same and returns phase 2 only. Not thread-safe.
  */
-int int8mm_timing_enable(int enable);
+int int8mm_timing_enable(int mode);
 int int8mm_timing_read(double* total_ms, int64_t* launches);
+int int8mm_timing_read_phases(double* ms /*[3]*/, int64_t* launches /*[3]*/);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ _f32 = ctypes.c_float
 # name -> (restype, argtypes); exactly the symbols include/int8mm.h declares
 SIGNATURES = {
     "int8_prepare_weight": (_int, [_p, _i64, _i64, _int, _p, _p, _p]),
+    "int8_tile_weight": (_int, [_p, _i64, _i64, _p, _p]),
     "int8_quant_rows": (_int, [_p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _i64, _p]),
     "int8_prepared_weight_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_mixed_matmul_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
@@ -44,6 +45,7 @@ SIGNATURES = {
     "int8mm_strerror": (ctypes.c_char_p, [_int]),
     "int8mm_timing_enable": (_int, [_int]),
     "int8mm_timing_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "int8mm_timing_read_phases": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
 }
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_ALIGN", 4: "E_THRESHOLD",
@@ -156,6 +158,22 @@ def prepare_weight(W: torch.Tensor, layout: int = 0):
     _check(lib().int8_prepare_weight(W.data_ptr(), K, N, layout, Wq.data_ptr(), a_w.data_ptr(),
                                      _stream(W)), "int8_prepare_weight")
     return Wq, a_w
+
+
+def tile_weight(Wq_nk: torch.Tensor) -> torch.Tensor:
+    """An already-quantized int8 weight [N, K] (row-major) -> the unit-tiled tensor the
+    matmul calls take, (N // 16, ceil(K / 64), 16, 64); pair it with the weight's own fp32
+    column constants [N]. Layout only (int8_tile_weight)."""
+    _need(Wq_nk, torch.int8, "Wq_nk")
+    if Wq_nk.dim() != 2:
+        raise ValueError(f"Wq_nk must be 2-D [N, K], got shape {tuple(Wq_nk.shape)}")
+    N, K = Wq_nk.shape
+    if N % 16 or K % 16:
+        raise ValueError("N and K must be multiples of 16")
+    Wq = torch.empty((N // 16, (K + 63) // 64, 16, 64), dtype=torch.int8, device=Wq_nk.device)
+    _check(lib().int8_tile_weight(Wq_nk.data_ptr(), K, N, Wq.data_ptr(), _stream(Wq_nk)),
+           "int8_tile_weight")
+    return Wq
 
 
 def untile_weight(Wq: torch.Tensor, K: int) -> torch.Tensor:
@@ -335,8 +353,10 @@ def read_status(workspace: torch.Tensor) -> tuple[int, int]:
     return rc, n.value
 
 
-def timing_enable(on: bool = True) -> None:
-    lib().int8mm_timing_enable(1 if on else 0)
+def timing_enable(on: bool | int = True) -> None:
+    """Event timing of each call's kernels: False/0 off, True/1 the main kernel, 2 also the
+    outlier-mask and row-quantization kernels (see int8mm_timing_enable)."""
+    _check(lib().int8mm_timing_enable(int(on)), "int8mm_timing_enable")
 
 
 def timing_read() -> tuple[float, int]:
@@ -345,3 +365,15 @@ def timing_read() -> tuple[float, int]:
     n = _i64(0)
     _check(lib().int8mm_timing_read(ctypes.byref(ms), ctypes.byref(n)), "int8mm_timing_read")
     return ms.value, n.value
+
+
+PHASES = ("outlier_mask", "quant_rows", "main")
+
+
+def timing_read_phases() -> dict:
+    """{phase: (summed milliseconds, launches)} since the last read, for the outlier-mask,
+    row-quantization and main kernels."""
+    ms = (ctypes.c_double * 3)()
+    n = (_i64 * 3)()
+    _check(lib().int8mm_timing_read_phases(ms, n), "int8mm_timing_read_phases")
+    return {p: (ms[i], n[i]) for i, p in enumerate(PHASES)}

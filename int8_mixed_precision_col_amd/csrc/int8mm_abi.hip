@@ -78,25 +78,35 @@ Layout layout(int64_t M, int64_t K, int64_t N, int64_t max_outliers) {
 // The weight side needs no scratch: a fixed, reserved size.
 constexpr size_t kQWorkspaceBytes = 256;
 
-// Optional event timing of the main kernel.
-bool g_timing = false;
-std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+// Optional event timing (int8mm_timing_enable): mode 1 brackets the main kernel of each
+// call (the MFMA GEMM, the decode kernel, the weight-only kernel), mode 2 also the
+// outlier-mask and row-quantization kernels. Each record is an event pair and a phase.
+enum Phase { kPhaseMask = 0, kPhaseQuant = 1, kPhaseMain = 2, kPhases = 3 };
+int g_timing = 0;
+struct TimedLaunch {
+  hipEvent_t begin, end;
+  int phase;
+};
+std::vector<TimedLaunch> g_events;
 size_t g_events_used = 0;
 
-int timing_begin(hipStream_t s) {
-  if (!g_timing) return INT8MM_OK;
+bool timed(int phase) { return g_timing == 2 || (g_timing == 1 && phase == kPhaseMain); }
+
+int timing_begin(hipStream_t s, int phase = kPhaseMain) {
+  if (!timed(phase)) return INT8MM_OK;
   if (g_events_used == g_events.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return INT8MM_E_HIP;
     if (hipEventCreate(&b) != hipSuccess) return INT8MM_E_HIP;
-    g_events.emplace_back(a, b);
+    g_events.push_back({a, b, 0});
   }
-  return hipEventRecord(g_events[g_events_used].first, s) == hipSuccess ? INT8MM_OK : INT8MM_E_HIP;
+  g_events[g_events_used].phase = phase;
+  return hipEventRecord(g_events[g_events_used].begin, s) == hipSuccess ? INT8MM_OK : INT8MM_E_HIP;
 }
 
-int timing_end(hipStream_t s) {
-  if (!g_timing) return INT8MM_OK;
-  if (hipEventRecord(g_events[g_events_used].second, s) != hipSuccess) return INT8MM_E_HIP;
+int timing_end(hipStream_t s, int phase = kPhaseMain) {
+  if (!timed(phase)) return INT8MM_OK;
+  if (hipEventRecord(g_events[g_events_used].end, s) != hipSuccess) return INT8MM_E_HIP;
   ++g_events_used;
   return INT8MM_OK;
 }
@@ -165,6 +175,13 @@ int int8_prepare_weight(const void* W, int64_t K, int64_t N, int w_layout, int8_
   if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_absmax)) return INT8MM_E_ALIGN;
   return hip_status(i8mm::launch_prepare_weight(static_cast<const _Float16*>(W), int(K), int(N),
                                                 w_layout, Wq, w_absmax, stream));
+}
+
+int int8_tile_weight(const int8_t* Wq_nk, int64_t K, int64_t N, int8_t* Wq, hipStream_t stream) {
+  if (!Wq_nk || !Wq) return INT8MM_E_NULL;
+  if (bad_k(K) || bad_n(N)) return INT8MM_E_SHAPE;
+  if (!aligned16(Wq_nk) || !aligned16(Wq)) return INT8MM_E_ALIGN;
+  return hip_status(i8mm::launch_tile_weight(Wq_nk, int(K), int(N), Wq, stream));
 }
 
 int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t* Xq,
@@ -261,8 +278,10 @@ int run_mixed(const void* X, int64_t M, int64_t K, const int8_t* Wq, const float
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
   _Float16* wot = reinterpret_cast<_Float16*>(ws + L.wot);
 
+  if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
   if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
     return INT8MM_E_HIP;
+  if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
   i8mm::QuantRowsArgs q{};
   q.X = x; q.M = int(M); q.K = int(K);
   q.partial = partial; q.R = L.R;
@@ -271,7 +290,9 @@ int run_mixed(const void* X, int64_t M, int64_t K, const int8_t* Wq, const float
   q.max_outliers = int(max_outliers);
   q.Xo = xo; q.o_stride = L.o_stride;
   q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
+  if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
   if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
+  if ((rc = timing_end(stream, kPhaseQuant)) != INT8MM_OK) return rc;
 
   i8mm::GemmArgs g{};
   g.Wq = Wq; g.Xq = xq; g.M = int(M); g.N = int(N); g.K = int(K);
@@ -311,8 +332,11 @@ int int8_quantize_activations(const void* X, int64_t M, int64_t K, float thresho
   int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
   const _Float16* x = static_cast<const _Float16*>(X);
   uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
+  int rc;
+  if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
   if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
     return INT8MM_E_HIP;
+  if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
   i8mm::QuantRowsArgs q{};
   q.X = x; q.M = int(M); q.K = int(K);
   q.partial = partial; q.R = L.R;
@@ -322,7 +346,9 @@ int int8_quantize_activations(const void* X, int64_t M, int64_t K, float thresho
   q.count_out = status + 1; q.status_out = status;
   q.max_outliers = int(max_outliers);
   q.Xo = reinterpret_cast<_Float16*>(ws + L.xo); q.o_stride = L.o_stride;
-  return hip_status(i8mm::launch_quant_rows(q, stream));
+  if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
+  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream, kPhaseQuant);
 }
 
 int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_outliers,
@@ -443,24 +469,38 @@ const char* int8mm_strerror(int code) {
   }
 }
 
-int int8mm_timing_enable(int enable) {
-  g_timing = enable != 0;
+int int8mm_timing_enable(int mode) {
+  if (mode < 0 || mode > 2) return INT8MM_E_SHAPE;
+  g_timing = mode;
+  return INT8MM_OK;
+}
+
+int int8mm_timing_read_phases(double* ms, int64_t* launches) {
+  if (!ms || !launches) return INT8MM_E_NULL;
+  for (int p = 0; p < kPhases; ++p) {
+    ms[p] = 0.0;
+    launches[p] = 0;
+  }
+  for (size_t i = 0; i < g_events_used; ++i) {
+    if (hipEventSynchronize(g_events[i].end) != hipSuccess) return INT8MM_E_HIP;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, g_events[i].begin, g_events[i].end) != hipSuccess)
+      return INT8MM_E_HIP;
+    ms[g_events[i].phase] += t;
+    ++launches[g_events[i].phase];
+  }
+  g_events_used = 0;
   return INT8MM_OK;
 }
 
 int int8mm_timing_read(double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return INT8MM_E_NULL;
-  double sum = 0.0;
-  for (size_t i = 0; i < g_events_used; ++i) {
-    if (hipEventSynchronize(g_events[i].second) != hipSuccess) return INT8MM_E_HIP;
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, g_events[i].first, g_events[i].second) != hipSuccess)
-      return INT8MM_E_HIP;
-    sum += ms;
-  }
-  *total_ms = sum;
-  *launches = static_cast<int64_t>(g_events_used);
-  g_events_used = 0;
+  double ms[kPhases];
+  int64_t n[kPhases];
+  const int rc = int8mm_timing_read_phases(ms, n);
+  if (rc != INT8MM_OK) return rc;
+  *total_ms = ms[kPhaseMain];
+  *launches = n[kPhaseMain];
   return INT8MM_OK;
 }
 

@@ -11,6 +11,9 @@ namespace i8mm {
 hipError_t launch_prepare_weight(const _Float16* W, int K, int N, int layout, int8_t* Wq,
                                  float* a_w, hipStream_t s);
 
+// Layout only: int8 [N, K] row-major -> unit-tiled, K padding zeroed.
+hipError_t launch_tile_weight(const int8_t* Wnk, int K, int N, int8_t* Wq, hipStream_t s);
+
 // Column outlier flags: partial[rc * W + w] for row chunk rc < R, word w < W = ceil(K/32).
 hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
                                uint32_t* partial, hipStream_t s);

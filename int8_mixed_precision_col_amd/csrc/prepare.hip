@@ -114,6 +114,33 @@ __global__ __launch_bounds__(256) void k_quant_rows_nk(const _Float16* __restric
     *reinterpret_cast<v2u*>(Wq + unit_offset(n, c * 8, ks)) = v2u{0u, 0u};
 }
 
+// Layout only: an int8 [N, K] row-major matrix into the unit-tiled layout, the K
+// padding as zero bytes. Thread t writes the 16-byte piece t of the output: unit
+// t / 64 (group g = unit / KS, unit s = unit % KS), row (t / 4) % 16, bytes 16 (t % 4)
+// of the unit's 64; its source is row 16 g + that row, columns 64 s + 16 (t % 4) ..
+// + 15 (K is a multiple of 16, so a piece lies wholly inside K or wholly past it).
+__global__ __launch_bounds__(256) void k_tile_weight(const int8_t* __restrict__ Wnk, int K, int ks,
+                                                     int8_t* __restrict__ Wq, long pieces) {
+  const long t = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= pieces) return;
+  const long unit = t >> 6;
+  const int r = static_cast<int>((t >> 2) & 15), c = static_cast<int>(t & 3);
+  const long g = unit / ks;
+  const int su = static_cast<int>(unit - g * ks);
+  const int k = 64 * su + 16 * c;
+  v4u v = {0u, 0u, 0u, 0u};
+  if (k < K) v = *reinterpret_cast<const v4u*>(Wnk + (g * 16 + r) * static_cast<long>(K) + k);
+  *reinterpret_cast<v4u*>(Wq + t * 16) = v;
+}
+
+hipError_t launch_tile_weight(const int8_t* Wnk, int K, int N, int8_t* Wq, hipStream_t s) {
+  const int ks = unit_ks(K);
+  const long pieces = static_cast<long>(N) * ks * 4;
+  hipLaunchKernelGGL(k_tile_weight, dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, s,
+                     Wnk, K, ks, Wq, pieces);
+  return hipGetLastError();
+}
+
 hipError_t launch_prepare_weight(const _Float16* W, int K, int N, int layout, int8_t* Wq,
                                  float* a_w, hipStream_t s) {
   if (layout == 0) {

@@ -213,3 +213,14 @@ def test_noalloc_rejects_before_any_hip_call(L):
     # what the limit admits: every decode shape and the 6.7B-like FFN shape
     assert ws(8, 4096, 4096, 256) <= NOALLOC_SCRATCH_BYTES
     assert ws(2048, 4096, 16384, 256) <= NOALLOC_SCRATCH_BYTES
+
+
+def test_tile_weight_rejects(L):
+    tw = L.int8_tile_weight
+    assert tw(None, 64, 32, P, None) == E_NULL
+    assert tw(P, 64, 32, None, None) == E_NULL
+    assert tw(P, 40, 32, P, None) == E_SHAPE       # K not a multiple of 16
+    assert tw(P, 64, 24, P, None) == E_SHAPE       # N not a multiple of 16
+    assert tw(P, 133152, 32, P, None) == E_SHAPE   # past the int32 guard
+    assert tw(UNALIGNED, 64, 32, P, None) == E_ALIGN
+    assert tw(P, 64, 32, UNALIGNED, None) == E_ALIGN

@@ -47,6 +47,35 @@ def test_prepare_weight_bit_exact(K, N, layout):
     assert pad is None or not pad.any()
 
 
+@pytest.mark.parametrize("K,N", [(1024, 1024), (1040, 528), (16, 16), (4112, 80), (48, 32)])
+def test_tile_weight_round_trip(K, N):
+    """int8_tile_weight is layout only: the [N, K] view of a prepared weight, tiled again,
+    is the prepared weight byte for byte (K padding zero)."""
+    announce(f"tile_weight round trip K={K} N={N}")
+    Wq, _ = binding.prepare_weight(dev(weight(K + N + 5, K, N)))
+    again = binding.tile_weight(binding.untile_weight(Wq, K))
+    assert torch.equal(again, Wq)
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 4096, 1024), (300, 1040, 528), (24, 4096, 1040)])
+def test_imported_int8_weight(M, K, N):
+    """A weight handed over already in int8 ([N, K] codes with fp32 column constants, the
+    form a pre-quantized checkpoint takes): the oracle's own conversion, placed by
+    int8_tile_weight, gives the oracle's product (decode kernel, tiled GEMM and
+    weight-stream GEMM)."""
+    path = "decode" if binding.is_decode(M, K) else "prefill"
+    announce(f"imported int8 weight {path} M={M} K={K} N={N}")
+    X = planted(M + K + 7, M, K, n_dims=3)
+    W = weight(M + N + 7, K, N)
+    Wq_ref, aw_ref = oracle.prepare_weight(W)
+    ref = oracle.mixed_matmul(X, Wq_ref, aw_ref, 6.0)
+    Wq = binding.tile_weight(dev(Wq_ref))
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = binding.mixed_matmul(dev(X), Wq, dev(aw_ref), 6.0, 256, acc_out=acc)
+    assert np.array_equal(host(acc), ref["acc"])
+    check_y(host(Y), ref["Y"])
+
+
 # ------------------------------------------------------------------ quant rows
 
 def _quant_case(X, t, mo):
