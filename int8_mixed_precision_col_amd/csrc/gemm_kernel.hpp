@@ -132,6 +132,28 @@ __device__ __forceinline__ char* stage_buf() {
   return buf;
 }
 
+// The LDS slice of wave w for staging its fp16 output sub-tile (WTM rows of WTN halves):
+// slices are packed into the ring's stages, as many per stage as fit.
+template <class C>
+__device__ __forceinline__ char* wave_slice(int w) {
+  constexpr int PW = C::WTM * C::WTN * 2, PER = C::STAGE / PW;
+  static_assert(PER >= 1 && C::NW <= PER * C::STAGES, "the ring holds every wave's output");
+  const int st = w / PER, off = (w % PER) * PW;
+  if constexpr (C::STAGES > 3)
+    if (st == 3) return stage_buf<C, 3>() + off;
+  if constexpr (C::STAGES > 2)
+    if (st == 2) return stage_buf<C, 2>() + off;
+  return (st == 1 ? stage_buf<C, 1>() : stage_buf<C, 0>()) + off;
+}
+// Chunk swizzle of a staged output row: spreads the 32 rows written by one fragment store
+// (one 16-byte chunk each) over 16 distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int ysw(int r) {
+  static_assert(CH == 16 || CH == 8, "staged row width");
+  if constexpr (CH == 16) return r & 15;
+  else return (r >> 1) & 7;
+}
+
 // Epilogue. 32x32 accumulator layout: lane l, register r holds column m = l % 32 and
 // row n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). The tile's
 // a_w / a_x and the outlier fragments (16 columns of W^ and Xo per pass) are staged
@@ -225,28 +247,41 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
       }
     }
   }
+  // Y: each wave rounds its sub-tile to fp16 into a private slice of the ring (free now:
+  // the barrier below also retires the staged scales and outlier fragments), then stores
+  // whole row segments, 16 bytes per lane and 64 / CH rows per instruction. Straight from
+  // the accumulator layout every store would cover 32 rows x 16 bytes, four times the
+  // memory requests for the same bytes.
+  lds_barrier();
+  char* ys = wave_slice<C>(wn + C::WGN * wm);
+  constexpr int CH = C::WTN / 8;   // 16-byte chunks per staged row
+  constexpr int RB = C::WTN * 2;   // staged row bytes
 #pragma unroll
   for (int i = 0; i < C::BN; ++i) {
-    const int nl = wn * C::WTN + i * 32;
 #pragma unroll
     for (int j = 0; j < C::BM; ++j) {
-      const int m = m0 + wm * C::WTM + j * 32 + l32;
-      if (m < M) {
-        const v16f y = __builtin_bit_cast(v16f, acc[i][j]);
+      const int r = j * 32 + l32;
+      const v16f y = __builtin_bit_cast(v16f, acc[i][j]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + nl + 8 * q + 4 * lhi;
-          if (n < N) {
-            v4h out;
+      for (int q = 0; q < 4; ++q) {
+        v4h out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              out[e] = overflow ? static_cast<_Float16>(__builtin_nanf(""))
-                                : static_cast<_Float16>(y[4 * q + e]);
-            *reinterpret_cast<v4h*>(g.Y + static_cast<size_t>(m) * N + n) = out;
-          }
-        }
+        for (int e = 0; e < 4; ++e)
+          out[e] = overflow ? static_cast<_Float16>(__builtin_nanf(""))
+                            : static_cast<_Float16>(y[4 * q + e]);
+        *reinterpret_cast<v4h*>(ys + r * RB + 16 * ((4 * i + q) ^ ysw<CH>(r)) + 8 * lhi) = out;
       }
     }
+  }
+  constexpr int RPI = 64 / CH;     // rows per store instruction
+  const int c = lane % CH;
+  const int n = n0 + wn * C::WTN + 8 * c;
+#pragma unroll
+  for (int t = 0; t < C::WTM / RPI; ++t) {
+    const int r = t * RPI + lane / CH;
+    const v4u v = *reinterpret_cast<const v4u*>(ys + r * RB + 16 * (c ^ ysw<CH>(r)));
+    const int m = m0 + wm * C::WTM + r;
+    if (m < M && n < N) *reinterpret_cast<v4u*>(g.Y + static_cast<size_t>(m) * N + n) = v;
   }
 }
 
