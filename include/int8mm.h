@@ -199,6 +199,18 @@ int int8_mixed_matmul_is_decode(int64_t M, int64_t K);
  * call; arguments are validated as for int8_mixed_matmul.
  */
 size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers);
+/*
+ * Where the quantization results sit inside a state buffer of int8_quant_state_bytes(M,
+ * K, max_outliers) bytes, so that a caller can read them: on success out[] holds byte
+ * offsets from the start of the state, out[0] a_x (fp32 [M], the row constants), out[1]
+ * Xq (int8, unit-tiled like a prepared weight with M rows: rows padded to a multiple of
+ * 16, K to a multiple of 64), out[2] Xo (fp16 [M][out[5]], the outlier columns' values
+ * in rank order, zeros past the count), out[3] the ascending outlier column list
+ * (int32 [max_outliers]; the first min(count, max_outliers) are valid), out[4] the
+ * outlier count (int32), and out[5] is Xo's row stride in elements. Host-only: no
+ * device access. Returns INT8MM_E_NULL for a null out, INT8MM_E_SHAPE for bad sizes.
+ */
+int int8_quant_state_layout(int64_t M, int64_t K, int64_t max_outliers, int64_t out[6]);
 int int8_quantize_activations(const void* X, int64_t M, int64_t K, float threshold,
                               int64_t max_outliers, void* state, size_t state_bytes,
                               hipStream_t stream);
@@ -264,11 +276,14 @@ const char* int8mm_strerror(int code);
 /*
  * Optional event timing, for benchmarks. int8mm_timing_enable(mode): 0 off; 1: each call
  * records a HIP event pair on its stream around its main kernel (the MFMA GEMM, the
- * decode kernel or the weight-only kernel); 2: also around the outlier-mask and
- * row-quantization kernels. Other modes are INT8MM_E_SHAPE. Not for calls under graph
+ * decode kernel or the weight-only kernel); 2: also around the two activation
+ * quantization kernels. Other modes are INT8MM_E_SHAPE. Not for calls under graph
  * capture (the events would be captured). int8mm_timing_read_phases synchronises on the
- * recorded events and returns, per phase (0 outlier mask, 1 row quantization, 2 main
- * kernel), the summed milliseconds and launch counts since the last read, then starts a
+ * recorded events and returns, per phase, the summed milliseconds and launch counts
+ * since the last read: phase 0 is the pass over X (flags, provisional row constants and
+ * codes; for K > 32768 the outlier-mask kernel), phase 1 the fix-up (outlier list, the
+ * rows it changes, outlier gathers; for K > 32768 the row-quantization kernel), phase 2
+ * the main kernel. It then starts a
  * new period; int8mm_timing_read does the same and returns phase 2 only. Not thread-safe.
  */
 int int8mm_timing_enable(int mode);

@@ -34,6 +34,7 @@ SIGNATURES = {
     "int8_mixed_matmul_is_decode": (_int, [_i64, _i64]),
     "int8_weight_only_matmul": (_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
     "int8_quant_state_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "int8_quant_state_layout": (ctypes.c_int, [_i64, _i64, _i64, ctypes.POINTER(_i64)]),
     "int8_quantize_activations": (_int, [_p, _i64, _i64, _f32, _i64, _p, ctypes.c_size_t, _p]),
     "int8_mixed_matmul_q_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_mixed_matmul_q": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, ctypes.c_size_t,
@@ -291,6 +292,22 @@ class QuantizedActivations:
                                                max_outliers, self.state.data_ptr(), nbytes,
                                                _stream(X)), "int8_quantize_activations")
 
+    def contents(self) -> dict:
+        """Views of the quantization results inside the state: a_x [M] fp32, Xq [M, K]
+        int8 (a row-major copy), Xo [M, o_stride] fp16, idx [max_outliers] int32 and
+        count (int)."""
+        off = (_i64 * 6)()
+        _check(lib().int8_quant_state_layout(self.M, self.K, self.max_outliers, off),
+               "int8_quant_state_layout")
+        st, M, K = self.state, self.M, self.K
+        ks, rows = (K + 63) // 64, (M + 15) // 16 * 16
+        a_x = st[off[0]:off[0] + 4 * M].view(torch.float32)
+        xq = st[off[1]:off[1] + rows * ks * 64].view(torch.int8).view(rows // 16, ks, 16, 64)
+        xo = st[off[2]:off[2] + 2 * M * off[5]].view(torch.float16).view(M, off[5])
+        idx = st[off[3]:off[3] + 4 * self.max_outliers].view(torch.int32)
+        count = int(st[off[4]:off[4] + 4].view(torch.int32).cpu()[0])
+        return {"a_x": a_x, "Xq": untile_weight(xq, K)[:M], "Xo": xo, "idx": idx, "count": count}
+
     def matmul(self, Wq: torch.Tensor, a_w: torch.Tensor, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None,
                acc_out: torch.Tensor | None = None) -> torch.Tensor:
@@ -367,12 +384,12 @@ def timing_read() -> tuple[float, int]:
     return ms.value, n.value
 
 
-PHASES = ("outlier_mask", "quant_rows", "main")
+PHASES = ("quant_pass", "quant_fixup", "main")
 
 
 def timing_read_phases() -> dict:
-    """{phase: (summed milliseconds, launches)} since the last read, for the outlier-mask,
-    row-quantization and main kernels."""
+    """{phase: (summed milliseconds, launches)} since the last read, for the pass over X,
+    the quantization fix-up and the main kernel (see int8mm_timing_read_phases)."""
     ms = (ctypes.c_double * 3)()
     n = (_i64 * 3)()
     _check(lib().int8mm_timing_read_phases(ms, n), "int8mm_timing_read_phases")

@@ -39,23 +39,39 @@ int mask_row_chunks(int64_t M, int64_t K) {
 
 struct Layout {
   size_t status = 0, partial = 0, a_x = 0, xq = 0, xo = 0, idx = 0, wot = 0, total = 0;
+  size_t lists = 0, masks = 0, jstar = 0, gmask = 0;  // one-pass quantization's scratch
   int R = 1, o_stride = 0;
+  bool fused = false;  // one pass over X and a fix-up, else the two-launch path
+  int rows_per_block = 0, nblk = 0;
 };
 
 // Quantized-activation state (int8_quantize_activations): [status, count] header, the
-// row-chunk column flags, a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and the
-// ascending outlier column list, each 256-byte aligned. The one-call workspace
-// (prefill) is the same followed by WoT, the outlier columns' weights gathered by the
-// row-quantization kernel's spare blocks; the quantize-once calls have none, and their
-// GEMM epilogue dequantizes those weights from Wq itself.
+// quantization scratch (one-pass path: the pass-1 blocks' published column lists and
+// masks and the per-row candidate columns; two-launch path: the row-chunk column
+// flags), a_x, unit-tiled Xq (rows padded to 16, K to 64), Xo and the ascending outlier
+// column list, each 256-byte aligned. The one-call workspace (prefill) is the same
+// followed by WoT, the outlier columns' weights gathered by the quantization's spare
+// blocks; the quantize-once calls have none, and their GEMM epilogue dequantizes those
+// weights from Wq itself.
 Layout prefill_layout(int64_t M, int64_t K, int64_t max_outliers) {
   Layout L;
   size_t off = 256;
   const size_t W = (K + 31) / 32;
   const size_t m_rows = (M + 15) & ~int64_t(15);
-  L.R = mask_row_chunks(M, K);
   L.o_stride = static_cast<int>((max_outliers + 15) & ~int64_t(15));
-  L.partial = off; off += round256(size_t(L.R) * W * 4);
+  L.fused = i8mm::quant_fused_supported(K);
+  if (L.fused) {
+    i8mm::quant_fused_geometry(M, K, &L.rows_per_block, &L.nblk);
+    // sized for min(M, kFusedMaxBlocks) >= nblk blocks, so that the size grows with M
+    const size_t nb = size_t(M < i8mm::kFusedMaxBlocks ? M : i8mm::kFusedMaxBlocks);
+    L.lists = off; off += round256(nb * (4 + i8mm::kFlagListCap) * 4);
+    L.masks = off; off += round256(nb * W * 4);
+    L.jstar = off; off += round256(size_t(M) * 16);
+    L.gmask = off; off += round256(W * 4);
+  } else {
+    L.R = mask_row_chunks(M, K);
+    L.partial = off; off += round256(size_t(L.R) * W * 4);
+  }
   L.a_x = off;     off += round256(size_t(M) * 4);
   L.xq = off;      off += round256(m_rows * i8mm::unit_ks(int(K)) * i8mm::kUnitK);
   L.xo = off;      off += round256(size_t(M) * L.o_stride * 2);
@@ -125,6 +141,56 @@ int check_mixed_args(const void* X, int64_t M, int64_t K, const int8_t* Wq,
       (acc_i32 && !aligned16(acc_i32)))
     return INT8MM_E_ALIGN;
   return INT8MM_OK;
+}
+
+// Activation quantization into the state at ws (layout L): the outlier column list and
+// count, a_x, unit-tiled Xq and Xo, plus WoT when wot is given (the one-call path). The
+// two kernels are timed as phases 0 and 1.
+int quantize_into(const _Float16* x, int64_t M, int64_t K, float threshold, int64_t max_outliers,
+                  char* ws, const Layout& L, const int8_t* Wq, const float* w_absmax, int64_t N,
+                  _Float16* wot, hipStream_t stream) {
+  int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+  int rc;
+  if (L.fused) {
+    i8mm::FusedQuantArgs f{};
+    f.X = x; f.M = int(M); f.K = int(K); f.t = threshold;
+    f.Xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    f.a_x = reinterpret_cast<float*>(ws + L.a_x);
+    f.jstar = reinterpret_cast<int32_t*>(ws + L.jstar);
+    f.lists = reinterpret_cast<int32_t*>(ws + L.lists);
+    f.masks = reinterpret_cast<uint32_t*>(ws + L.masks);
+    f.rows_per_block = L.rows_per_block; f.nblk = L.nblk;
+    f.gmask = reinterpret_cast<uint32_t*>(ws + L.gmask);
+    f.idx_out = max_outliers > 0 ? reinterpret_cast<int32_t*>(ws + L.idx) : nullptr;
+    f.count_out = status + 1; f.status_out = status;
+    f.max_outliers = int(max_outliers);
+    f.Xo = reinterpret_cast<_Float16*>(ws + L.xo); f.o_stride = L.o_stride;
+    f.Wq = Wq; f.a_w = w_absmax; f.N = int(N); f.WoT = wot;
+    if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
+    if (i8mm::launch_quant_pass(f, stream) != hipSuccess) return INT8MM_E_HIP;
+    if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
+    if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
+    if (i8mm::launch_quant_fixup(f, stream) != hipSuccess) return INT8MM_E_HIP;
+    return timing_end(stream, kPhaseQuant);
+  }
+  uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
+  if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
+  if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
+    return INT8MM_E_HIP;
+  if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
+  i8mm::QuantRowsArgs q{};
+  q.X = x; q.M = int(M); q.K = int(K);
+  q.partial = partial; q.R = L.R;
+  q.Xq = reinterpret_cast<int8_t*>(ws + L.xq); q.xq_tiled = 1;
+  q.a_x = reinterpret_cast<float*>(ws + L.a_x);
+  q.idx_out = max_outliers > 0 ? reinterpret_cast<int32_t*>(ws + L.idx) : nullptr;
+  q.count_out = status + 1; q.status_out = status;
+  q.max_outliers = int(max_outliers);
+  q.Xo = reinterpret_cast<_Float16*>(ws + L.xo); q.o_stride = L.o_stride;
+  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
+  if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
+  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
+  return timing_end(stream, kPhaseQuant);
 }
 
 // The whole decomposed product into a workspace of layout(M, K, N, max_outliers).total
@@ -271,28 +337,14 @@ int run_mixed(const void* X, int64_t M, int64_t K, const int8_t* Wq, const float
     return timing_end(stream);
   }
 
-  uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
   float* a_x = reinterpret_cast<float*>(ws + L.a_x);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
   _Float16* xo = reinterpret_cast<_Float16*>(ws + L.xo);
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
   _Float16* wot = reinterpret_cast<_Float16*>(ws + L.wot);
-
-  if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
-  if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
-    return INT8MM_E_HIP;
-  if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
-  i8mm::QuantRowsArgs q{};
-  q.X = x; q.M = int(M); q.K = int(K);
-  q.partial = partial; q.R = L.R;
-  q.Xq = xq; q.xq_tiled = 1; q.a_x = a_x;
-  q.idx_out = max_outliers > 0 ? idx : nullptr; q.count_out = status + 1; q.status_out = status;
-  q.max_outliers = int(max_outliers);
-  q.Xo = xo; q.o_stride = L.o_stride;
-  q.Wq = Wq; q.a_w = w_absmax; q.N = int(N); q.WoT = wot;
-  if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
-  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
-  if ((rc = timing_end(stream, kPhaseQuant)) != INT8MM_OK) return rc;
+  if ((rc = quantize_into(x, M, K, threshold, max_outliers, ws, L, Wq, w_absmax, N, wot,
+                          stream)) != INT8MM_OK)
+    return rc;
 
   i8mm::GemmArgs g{};
   g.Wq = Wq; g.Xq = xq; g.M = int(M); g.N = int(N); g.K = int(K);
@@ -314,6 +366,19 @@ size_t int8_quant_state_bytes(int64_t M, int64_t K, int64_t max_outliers) {
   return prefill_layout(M, K, max_outliers).total;
 }
 
+int int8_quant_state_layout(int64_t M, int64_t K, int64_t max_outliers, int64_t out[6]) {
+  if (!out) return INT8MM_E_NULL;
+  if (bad_m(M) || bad_k(K) || bad_outliers(max_outliers, K)) return INT8MM_E_SHAPE;
+  const Layout L = prefill_layout(M, K, max_outliers);
+  out[0] = int64_t(L.a_x);
+  out[1] = int64_t(L.xq);
+  out[2] = int64_t(L.xo);
+  out[3] = int64_t(L.idx);
+  out[4] = int64_t(L.status) + 4;
+  out[5] = L.o_stride;
+  return INT8MM_OK;
+}
+
 size_t int8_mixed_matmul_q_workspace_bytes(int64_t N, int64_t max_outliers) {
   if (bad_n(N) || max_outliers < 0 || max_outliers > kMaxOutliers) return 0;
   return kQWorkspaceBytes;
@@ -328,27 +393,8 @@ int int8_quantize_activations(const void* X, int64_t M, int64_t K, float thresho
   if (!aligned16(X) || !aligned16(state)) return INT8MM_E_ALIGN;
   const Layout L = prefill_layout(M, K, max_outliers);
   if (state_bytes < L.total) return INT8MM_E_WORKSPACE;
-  char* ws = static_cast<char*>(state);
-  int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
-  const _Float16* x = static_cast<const _Float16*>(X);
-  uint32_t* partial = reinterpret_cast<uint32_t*>(ws + L.partial);
-  int rc;
-  if ((rc = timing_begin(stream, kPhaseMask)) != INT8MM_OK) return rc;
-  if (i8mm::launch_outlier_mask(x, int(M), int(K), threshold, L.R, partial, stream) != hipSuccess)
-    return INT8MM_E_HIP;
-  if ((rc = timing_end(stream, kPhaseMask)) != INT8MM_OK) return rc;
-  i8mm::QuantRowsArgs q{};
-  q.X = x; q.M = int(M); q.K = int(K);
-  q.partial = partial; q.R = L.R;
-  q.Xq = reinterpret_cast<int8_t*>(ws + L.xq); q.xq_tiled = 1;
-  q.a_x = reinterpret_cast<float*>(ws + L.a_x);
-  q.idx_out = max_outliers > 0 ? reinterpret_cast<int32_t*>(ws + L.idx) : nullptr;
-  q.count_out = status + 1; q.status_out = status;
-  q.max_outliers = int(max_outliers);
-  q.Xo = reinterpret_cast<_Float16*>(ws + L.xo); q.o_stride = L.o_stride;
-  if ((rc = timing_begin(stream, kPhaseQuant)) != INT8MM_OK) return rc;
-  if (i8mm::launch_quant_rows(q, stream) != hipSuccess) return INT8MM_E_HIP;
-  return timing_end(stream, kPhaseQuant);
+  return quantize_into(static_cast<const _Float16*>(X), M, K, threshold, max_outliers,
+                       static_cast<char*>(state), L, nullptr, nullptr, 0, nullptr, stream);
 }
 
 int int8_mixed_matmul_q(const void* state, int64_t M, int64_t K, int64_t max_outliers,

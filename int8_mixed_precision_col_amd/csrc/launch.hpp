@@ -40,6 +40,47 @@ struct QuantRowsArgs {
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s);
 
+// One pass over X for the outlier flags, a provisional row constant and provisional
+// codes (launch_quant_pass), then a small fix-up (launch_quant_fixup: a launch that ORs
+// the blocks' flags into the column set, then one for the rows it changes and the
+// gathers).
+constexpr int kFlagListCap = 64;      // columns a pass-1 block lists before it stores
+                                      // its whole flag mask instead
+constexpr int kFixZeroMax = 64;       // more outlier columns than this: every row is
+                                      // requantized in the fix-up rather than patched
+constexpr int kFusedMaxChunks = 16;   // 8-half chunks per thread: K <= 32768
+constexpr int kFusedMaxBlocks = 1024; // pass-1 blocks at most
+struct FusedQuantArgs {
+  const _Float16* X;
+  int M, K;
+  float t;
+  int8_t* Xq;           // unit-tiled [M (padded to 16)][K (padded to 64)]
+  float* a_x;           // [M]: provisional after pass 1, final after the fix-up
+  int32_t* jstar;       // [M][4]: per wave of the row's block, a column reaching the
+                        // provisional constant, or -1
+  int32_t* lists;       // [nblk][1 + kFlagListCap]: flagged-column count (-1: see masks),
+                        // then the columns
+  uint32_t* masks;      // [nblk][ceil(K / 32)]: a block's flags when it lists too many
+  int rows_per_block, nblk;
+  uint32_t* gmask;      // [ceil(K / 32)]: the outlier columns (cleared by pass 1, ORed
+                        // by the fix-up's first launch)
+  int32_t* idx_out;     // [max_outliers] ascending outlier columns, nullable
+  int32_t* count_out;   // [1]
+  int32_t* status_out;  // [1], nullable
+  int max_outliers;
+  _Float16* Xo;         // nullable [M][o_stride]
+  int o_stride;
+  const int8_t* Wq;     // WoT gather as in QuantRowsArgs (nullable = none)
+  const float* a_w;
+  int N;
+  _Float16* WoT;
+};
+bool quant_fused_supported(int64_t K);
+// Pass-1 blocks for M rows of K columns, and the rows each takes.
+void quant_fused_geometry(int64_t M, int64_t K, int* rows_per_block, int* nblk);
+hipError_t launch_quant_pass(const FusedQuantArgs& a, hipStream_t s);
+hipError_t launch_quant_fixup(const FusedQuantArgs& a, hipStream_t s);
+
 struct GemmArgs {
   const int8_t* Wq;   // unit-tiled [N][K]
   const int8_t* Xq;   // unit-tiled [M][K] (rows padded to a multiple of 16)

@@ -79,19 +79,17 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
 // packed u16 magnitude max reduced over the wave with DPP, and the codes come from the
 // bracketing pair of fused multiply-adds (quant8_fast); groups where the pair
 // disagrees take quant8_exact.
-// Loads a row into registers for quant_one_row<CH> (CH > 0): chunk c = lane + 64 i;
-// unconditional loads at clamped addresses, zeros past the row.
-// (STRIDE threads share the row: chunk c = t + STRIDE i.)
+// Loads a row into registers for quant_one_row<CH> (CH > 0): chunk c = t + STRIDE i
+// (STRIDE threads share the row), through a buffer resource over the row so that chunks
+// past its end read as zeros. (A select of the loaded value against zero would make
+// each load wait for its data before the next one issues.)
 template <int CH, int STRIDE = 64>
 __device__ __forceinline__ void load_row(const _Float16* __restrict__ xr, int K, int t,
                                          v8h (&v)[CH > 0 ? CH : 1]) {
-  const int nchunk = K >> 3;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(xr, static_cast<unsigned>(K) * 2u);
 #pragma unroll
-  for (int i = 0; i < (CH > 0 ? CH : 1); ++i) {
-    const int c = t + STRIDE * i;
-    const v8h t = *reinterpret_cast<const v8h*>(xr + min(c, nchunk - 1) * 8);
-    v[i] = c < nchunk ? t : v8h{};
-  }
+  for (int i = 0; i < (CH > 0 ? CH : 1); ++i)
+    v[i] = __builtin_bit_cast(v8h, buf_load16(rs, static_cast<unsigned>(t + STRIDE * i) * 16u));
 }
 
 template <int CH>
@@ -347,6 +345,441 @@ hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t s) {
     else I8MM_QR(0, false);
   }
 #undef I8MM_QR
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// One pass over X (k_quant_pass), then a two-launch fix-up (k_quant_or, k_quant_fix).
+//
+// The outlier set O is global (a column is an outlier when any row reaches t), yet a
+// row needs O only to leave columns out of its constant and its codes. Pass 1 therefore
+// quantizes each row, as it streams by, under the provisional constant
+// a' = max{|x| : |x| < t} of that row, its own flagged entries cleared. a' bounds the
+// exact constant a = max{|x_j| : j not in O} from above, and equals it whenever some
+// column where the row reaches a' is not in O: then every code already is the exact one,
+// except at outlier columns flagged only by other rows, which must become 0. Each block
+// ORs the flags of its rows into an LDS column mask and publishes it (a short ascending
+// column list, or the whole mask). k_quant_or ORs the published flags into the call's
+// mask of O; each k_quant_fix block ranks O and, per row, either zeroes the provisional
+// codes at the outlier columns or, when every column that reached a' is an outlier (or
+// O is too large to patch), reads the row again and requantizes it under the exact
+// mask. Either way the codes, the row constants and the ranked column list are those of
+// the two-launch path above.
+
+bool quant_fused_supported(int64_t K) { return K <= 256 * 8 * kFusedMaxChunks; }
+
+// Enough pass-1 blocks to fill the chip once: 256 CUs times the blocks one CU holds at
+// the kernel's register use for this row length (a block's rows are a serial chain of
+// load latencies, so fewer rows per block is faster while the blocks still fit), at
+// most kFusedMaxBlocks (every fix-up block reads every block's published flags).
+void quant_fused_geometry(int64_t M, int64_t K, int* rows_per_block, int* nblk) {
+  const int64_t per = (K / 8 + 255) / 256;
+  const int64_t per_cu = per <= 2 ? 8 : per <= 4 ? 5 : per <= 6 ? 4 : per <= 8 ? 3 : per <= 12 ? 2 : 1;
+  int64_t target = 256 * per_cu;
+  if (target > kFusedMaxBlocks) target = kFusedMaxBlocks;
+  const int64_t rpb = (M + target - 1) / target;
+  *rows_per_block = static_cast<int>(rpb);
+  *nblk = static_cast<int>((M + rpb - 1) / rpb);
+}
+
+constexpr int kListSlot = 4 + kFlagListCap;  // ints per published list: count, 3 pad, columns
+
+// Block b: rows [b * rows_per_block, ...), each held by the whole block (thread t takes
+// chunks t + 256 i), the next row's loads in flight while the current one is processed.
+template <int CH>
+__global__ __launch_bounds__(256) void k_quant_pass(FusedQuantArgs a) {
+  extern __shared__ uint32_t mask_s[];  // the block's column flags, ceil(K / 32) words
+  __shared__ unsigned red_s[2][4];
+  __shared__ int tot_s[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, W = (K + 31) >> 5, nchunk = K >> 3, ks = unit_ks(K);
+  const unsigned tb = threshold_bits(a.t);
+  for (int w = tid; w < W; w += 256) mask_s[w] = 0u;
+  // block 0 clears the call's outlier mask, which the fix-up's first launch ORs into
+  if (blockIdx.x == 0)
+    for (int w = tid; w < W; w += 256) a.gmask[w] = 0u;
+  lds_barrier();
+  const int r0 = blockIdx.x * a.rows_per_block, r1 = min(a.M, r0 + a.rows_per_block);
+
+  auto process = [&](v8h (&v)[CH], int row, int par) {
+    // flags |x| >= t (rare: their halves are cleared and ORed into the block mask) and
+    // the largest kept magnitude, per chunk and over the row
+    unsigned cmx[CH];
+    unsigned pm = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
+      v4u u = __builtin_bit_cast(v4u, v[i]) & 0x7fff7fffu;
+      unsigned cm = pk_max_u16(pk_max_u16(u[0], u[1]), pk_max_u16(u[2], u[3]));
+      if (max(cm & 0xffffu, cm >> 16) >= tb && c < nchunk) {
+        unsigned fm = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          fm |= static_cast<unsigned>((u[d] & 0xffffu) >= tb) << (2 * d);
+          fm |= static_cast<unsigned>((u[d] >> 16) >= tb) << (2 * d + 1);
+        }
+        drop_halves(v[i], fm);
+        atomicOr(&mask_s[c >> 2], fm << ((c & 3) << 3));
+        u = __builtin_bit_cast(v4u, v[i]) & 0x7fff7fffu;
+        cm = pk_max_u16(pk_max_u16(u[0], u[1]), pk_max_u16(u[2], u[3]));
+      }
+      cmx[i] = max(cm & 0xffffu, cm >> 16);
+      pm = max(pm, cmx[i]);
+    }
+    const unsigned wm = wave_max_u32(pm);
+    if (lane == 0) red_s[par][wave] = wm;
+    lds_barrier();
+    const unsigned hm = max(max(red_s[par][0], red_s[par][1]), max(red_s[par][2], red_s[par][3]));
+    const float m = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(hm)));
+    const QuantBracket br = quant_bracket(m);
+    // codes under a' (K padding included: those chunks hold zeros), and the smallest
+    // column of this wave whose magnitude is a', kept as 0x7fffffff - column so that
+    // the wave's unsigned max finds it (0: none)
+    // Stores go through a buffer resource over the row's 16-row group, so that chunks
+    // past the K padding fall outside it and are dropped: every store is issued, and the
+    // compiler can count them when it waits for the next row's loads. (256 CH >= ks * 8
+    // always, since ks * 8 is nchunk rounded up to a multiple of 8 and 256 CH is it
+    // rounded up to a multiple of 256: the padding chunks are all covered here.)
+    const __amdgpu_buffer_rsrc_t qs =
+        make_rsrc(a.Xq + static_cast<size_t>(row >> 4) * ks * kUnitBytes,
+                  static_cast<unsigned>(ks) * kUnitBytes);
+    const unsigned row_off = static_cast<unsigned>(row & 15) * kUnitK;
+    unsigned best = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
+      unsigned dis;
+      v2u o = quant8_fast(v[i], br, dis);
+      if (dis) o = quant8_exact(v[i], m, br.lo);
+      __builtin_amdgcn_raw_buffer_store_b64(
+          o, qs, static_cast<int>((c >> 3) * kUnitBytes + row_off + (c & 7) * 8), 0, 0);
+      if (hm != 0u && cmx[i] == hm) {
+        const v4u u = __builtin_bit_cast(v4u, v[i]);
+        int e = 0;
+#pragma unroll
+        for (int d = 3; d >= 0; --d) {
+          if (((u[d] >> 16) & 0x7fffu) == hm) e = 2 * d + 1;
+          if ((u[d] & 0x7fffu) == hm) e = 2 * d;
+        }
+        best = max(best, 0x7fffffffu - static_cast<unsigned>(c * 8 + e));
+      }
+    }
+    const unsigned wb = wave_max_u32(best);
+    if (lane == 0)
+      a.jstar[static_cast<size_t>(row) * 4 + wave] = wb ? static_cast<int>(0x7fffffffu - wb) : -1;
+    if (tid == 0) a.a_x[row] = m;
+  };
+
+  // The next row's loads are always issued (past the block's last row they re-read it):
+  // loads under a condition make the compiler wait for them where the paths join.
+  if (r0 < r1) {
+    v8h A[CH], B[CH];
+    load_row<CH, 256>(a.X + static_cast<size_t>(r0) * K, K, tid, A);
+    for (int row = r0; row < r1; row += 2) {
+      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + 1, r1 - 1)) * K, K, tid, B);
+      process(A, row, 0);
+      if (row + 1 >= r1) break;
+      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + 2, r1 - 1)) * K, K, tid, A);
+      process(B, row + 1, 1);
+    }
+  }
+
+  // publish the block's flags: the column list (ascending) when short, else the whole
+  // mask. Thread t owns mask words [t*per, (t+1)*per); a block prefix sum places them.
+  lds_barrier();
+  const int per = (W + 255) / 256;
+  const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(mask_s[w]);
+  const int incl = wave_prefix_sum(mine);
+  if (lane == 63) tot_s[wave] = incl;
+  lds_barrier();
+  int before = incl - mine, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += i < wave ? tot_s[i] : 0;
+    total += tot_s[i];
+  }
+  int32_t* lst = a.lists + static_cast<size_t>(blockIdx.x) * kListSlot;
+  if (total <= kFlagListCap) {
+    for (int w = w0, r = before; w < w1; ++w) {
+      uint32_t bits = mask_s[w];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        lst[4 + r++] = w * 32 + b;
+      }
+    }
+    if (tid == 0) lst[0] = total;
+  } else {
+    uint32_t* msk = a.masks + static_cast<size_t>(blockIdx.x) * W;
+    for (int w = tid; w < W; w += 256) msk[w] = mask_s[w];
+    if (tid == 0) lst[0] = -1;
+  }
+}
+
+// The fix-up's first launch ORs the pass-1 blocks' flags into the call's outlier mask
+// (cleared by pass 1): thread t of block b reads the list published by pass-1 block
+// 256 b + t (its count and first 32 columns in one go; the slot is always there to read
+// and entries past the count are ignored; columns beyond 32 only when a list is longer),
+// or that block's whole mask when it listed too many, and ORs it into the block's LDS
+// copy of the mask; the block then ORs its nonzero words into the call's mask. A list
+// equal to list 0 is skipped (the lists are ascending, so equal column sets are equal
+// ints): most lists hold the same columns, whose atomics would all pile onto the same
+// few words. Dynamic LDS: ceil(K / 32) words.
+__global__ __launch_bounds__(256) void k_quant_or(FusedQuantArgs a) {
+  extern __shared__ uint32_t m_s[];
+  const int W = (a.K + 31) >> 5;
+  const int tid = threadIdx.x, pb = blockIdx.x * 256 + tid;
+  const int b = min(pb, a.nblk - 1);
+  const v4i* slot = reinterpret_cast<const v4i*>(a.lists + static_cast<size_t>(b) * kListSlot);
+  const v4i* ref = reinterpret_cast<const v4i*>(a.lists);
+  const v4i head = slot[0], rhead = ref[0];
+  v4i e[8], re[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    e[q] = slot[1 + q];
+    re[q] = ref[1 + q];
+  }
+  __shared__ int novf_s;
+  __shared__ int ovf_s[256];
+  for (int w = tid; w < W; w += 256) m_s[w] = 0u;
+  if (tid == 0) novf_s = 0;
+  lds_barrier();
+  auto set_bit = [&](int col) {
+    const uint32_t bit = 1u << (col & 31);
+    if (!(m_s[col >> 5] & bit)) atomicOr(&m_s[col >> 5], bit);
+  };
+  if (pb < a.nblk) {
+    const int h = head[0];
+    if (h < 0) ovf_s[atomicAdd(&novf_s, 1)] = pb;
+    bool same = pb > 0 && h >= 0 && h <= 32 && h == rhead[0];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (4 * q + k < h && e[q][k] != re[q][k]) same = false;
+    if (!same && h >= 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (4 * q + k < h) set_bit(e[q][k]);
+      for (int r = 32; r < h; ++r) set_bit(a.lists[static_cast<size_t>(pb) * kListSlot + 4 + r]);
+    }
+  }
+  lds_barrier();
+  // whole masks of the blocks that listed too many, a word per thread
+  const int nov = novf_s;
+  for (int i = 0; i < nov; ++i) {
+    const uint32_t* msk = a.masks + static_cast<size_t>(ovf_s[i]) * W;
+    for (int w = tid; w < W; w += 256) m_s[w] |= msk[w];
+  }
+  lds_barrier();
+  for (int w = tid; w < W; w += 256)
+    if (const uint32_t m = m_s[w]) atomicOr(&a.gmask[w], m);
+}
+
+// Blocks [0, nfix): rows 16 b .. 16 b + 15 (wave w patches rows 16 b + 4 r + w; rows to
+// requantize are collected and then done by the whole block, the row held in
+// registers, CH chunks per thread). Blocks from nfix on: the WoT gather, 64 weight rows
+// each (WoT rows n = 64 (b - nfix) + t % 64, ranks r = t / 64 + 4 j). Dynamic LDS: the
+// outlier mask (ceil(K / 32) words), then o_lds ranked columns.
+template <int CH>
+__global__ __launch_bounds__(256) void k_quant_fix(FusedQuantArgs a, int o_lds, int nfix) {
+  extern __shared__ uint32_t lds[];
+  const int K = a.K, W = (K + 31) >> 5, ks = unit_ks(K);
+  uint32_t* g_s = lds;
+  int* idx_s = reinterpret_cast<int*>(lds + W);
+  __shared__ int nredo_s;
+  __shared__ int redo_s[16];
+  __shared__ unsigned red_s[4];
+  __shared__ int wave_tot[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool row_block = static_cast<int>(blockIdx.x) < nfix;
+  // a_x and the candidate columns of the wave's rows go out with the column set's loads
+  const int rbase = blockIdx.x * 16 + wave;
+  float ax[4];
+  v4i js[4];
+  if (row_block) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = min(rbase + 4 * rr, a.M - 1);
+      ax[rr] = a.a_x[row];
+      js[rr] = *reinterpret_cast<const v4i*>(a.jstar + static_cast<size_t>(row) * 4);
+    }
+  }
+  // the outlier set: rank the mask's columns (thread t owns words [t*per, (t+1)*per))
+  for (int w = tid; w < W; w += 256) g_s[w] = a.gmask[w];
+  if (tid == 0) nredo_s = 0;
+  lds_barrier();
+  const int per = (W + 255) / 256;
+  const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(g_s[w]);
+  const int incl = wave_prefix_sum(mine);
+  if (lane == 63) wave_tot[wave] = incl;
+  lds_barrier();
+  int before = incl - mine, count = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += i < wave ? wave_tot[i] : 0;
+    count += wave_tot[i];
+  }
+  for (int w = w0, r = before; w < w1; ++w) {
+    uint32_t bits = g_s[w];
+    while (bits) {
+      const int bb = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (r < o_lds) idx_s[r] = w * 32 + bb;
+      ++r;
+    }
+  }
+  lds_barrier();
+  const int nr = min(count, o_lds);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      a.count_out[0] = count;
+      if (a.status_out) a.status_out[0] = count > a.max_outliers ? 7 : 0;
+    }
+    if (a.idx_out)
+      for (int r = tid; r < min(count, a.max_outliers); r += 256) a.idx_out[r] = idx_s[r];
+  }
+  const int o_pad = min((count + 15) & ~15, a.o_stride);
+  const _Float16* __restrict__ X = a.X;
+
+  if (row_block) {
+    // rows: patch (zero the provisional codes at every outlier column) when some column
+    // reaching the provisional constant is not an outlier, else requantize
+    const bool patch = count <= min(kFixZeroMax, o_lds);
+    bool redo[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = rbase + 4 * rr;
+      redo[rr] = row < a.M && !patch;
+      if (row < a.M && patch && count > 0 && ax[rr] > 0.0f) {
+        bool keep = false;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = js[rr][k];
+          keep = keep || (c >= 0 && !((g_s[c >> 5] >> (c & 31)) & 1u));
+        }
+        redo[rr] = !keep;
+      }
+      if (redo[rr] && lane == 0) redo_s[atomicAdd(&nredo_s, 1)] = row;
+    }
+    lds_barrier();
+    const int nredo = nredo_s;
+    // the outlier values of the wave's rows (for up to 64 ranks, all four rows' loads
+    // before any store: the pointers do not alias) and the zeroed codes
+    _Float16* __restrict__ Xo = a.Xo;
+    int8_t* __restrict__ Xq = a.Xq;
+    auto patch_rows = [&]() {
+      if (Xo && o_pad <= 64) {
+        const int col = lane < nr ? idx_s[lane] : 0;
+        _Float16 g[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = min(rbase + 4 * rr, a.M - 1);
+          g[rr] = lane < count ? X[static_cast<size_t>(row) * K + col] : _Float16(0);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = rbase + 4 * rr;
+          if (row < a.M && lane < o_pad) Xo[static_cast<size_t>(row) * a.o_stride + lane] = g[rr];
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = rbase + 4 * rr;
+        if (row >= a.M) break;
+        if (!redo[rr])
+          for (int r = lane; r < count; r += 64) Xq[unit_offset(row, idx_s[r], ks)] = 0;
+        if (Xo && o_pad > 64) {
+          const _Float16* xr = X + static_cast<size_t>(row) * K;
+          _Float16* xo = Xo + static_cast<size_t>(row) * a.o_stride;
+          for (int r = lane; r < o_pad; r += 64) xo[r] = r < count ? xr[idx_s[r]] : _Float16(0);
+        }
+      }
+    };
+    if (nredo == 0) {
+      patch_rows();
+    } else {
+      // the first row to requantize is loaded before the patching, under it (inside this
+      // branch: registers loaded under a condition and used after the join would make
+      // the compiler wait for them at the join)
+      v8h v[CH];
+      load_row<CH, 256>(X + static_cast<size_t>(redo_s[0]) * K, K, tid, v);
+      patch_rows();
+      for (int i = 0; i < nredo; ++i) {
+        const int row = redo_s[i];
+        const _Float16* xr = X + static_cast<size_t>(row) * K;
+        if (i > 0) load_row<CH, 256>(xr, K, tid, v);
+        quant_row_block<CH>(xr, K, g_s, Xq, row, ks, a.a_x + row, tid, v, red_s);
+        lds_barrier();  // red_s is reused by the next row
+      }
+    }
+  } else {
+    // WoT[n, r] = fp16(Wq[n, O_r] * a_w[n] / 127), as in k_quant_rows: thread t takes
+    // row n = 64 (b - nfix) + t % 64 and ranks t / 64 + 4 j, all its loads at once
+    const int n = (blockIdx.x - nfix) * 64 + lane;
+    if (n >= a.N) return;
+    const float aw = a.a_w[n];
+    const int8_t* __restrict__ Wq = a.Wq;
+    _Float16* __restrict__ dst = a.WoT + static_cast<size_t>(n) * a.o_stride;
+    for (int r0 = wave; r0 < o_pad; r0 += 64) {
+      int8_t q[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = r0 + 4 * j;
+        q[j] = r < count ? Wq[unit_offset(n, idx_s[min(r, o_lds - 1)], ks)] : int8_t(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = r0 + 4 * j;
+        if (r < o_pad)
+          dst[r] = static_cast<_Float16>(__fdiv_rn(static_cast<float>(q[j]) * aw, 127.0f));
+      }
+    }
+  }
+}
+
+hipError_t launch_quant_pass(const FusedQuantArgs& a, hipStream_t s) {
+  const int per = (a.K / 8 + 255) / 256;
+  const size_t lds = static_cast<size_t>((a.K + 31) / 32) * 4;
+#define I8MM_QP(CHV) hipLaunchKernelGGL((k_quant_pass<CHV>), dim3(a.nblk), dim3(256), lds, s, a)
+  if (per <= 1) I8MM_QP(1);
+  else if (per <= 2) I8MM_QP(2);
+  else if (per <= 4) I8MM_QP(4);
+  else if (per <= 6) I8MM_QP(6);
+  else if (per <= 8) I8MM_QP(8);
+  else if (per <= 10) I8MM_QP(10);
+  else if (per <= 12) I8MM_QP(12);
+  else I8MM_QP(16);
+#undef I8MM_QP
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fixup(const FusedQuantArgs& a, hipStream_t s) {
+  const int W = (a.K + 31) / 32;
+  const int o_lds = a.o_stride > a.max_outliers ? a.o_stride : a.max_outliers;
+  const size_t lds = static_cast<size_t>(W + o_lds) * 4;
+  hipLaunchKernelGGL(k_quant_or, dim3((a.nblk + 255) / 256), dim3(256), static_cast<size_t>(W) * 4,
+                     s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nfix = (a.M + 15) / 16;
+  const int ngather = a.WoT ? (a.N + 63) / 64 : 0;
+  const int per = (a.K / 8 + 255) / 256;
+  const dim3 grid(nfix + ngather), block(256);
+#define I8MM_QF(CHV) hipLaunchKernelGGL((k_quant_fix<CHV>), grid, block, lds, s, a, o_lds, nfix)
+  if (per <= 1) I8MM_QF(1);
+  else if (per <= 2) I8MM_QF(2);
+  else if (per <= 4) I8MM_QF(4);
+  else if (per <= 8) I8MM_QF(8);
+  else I8MM_QF(16);
+#undef I8MM_QF
   return hipGetLastError();
 }
 

@@ -73,6 +73,10 @@ int main() {
 
   // quantize once / grouped
   expect("state bytes bad", static_cast<long long>(int8_quant_state_bytes(INT64_MAX, 64, 4)), 0);
+  int64_t lay[6];
+  expect("state layout", int8_quant_state_layout(4096, 20480, 256, lay), INT8MM_OK);
+  expect("state layout null", int8_quant_state_layout(4096, 20480, 256, nullptr), INT8MM_E_NULL);
+  expect("state layout bad", int8_quant_state_layout(INT64_MAX, 64, 4, lay), INT8MM_E_SHAPE);
   expect("qa short", int8_quantize_activations(P, 64, 256, 6.0f, 16, P, 1, nullptr), INT8MM_E_WORKSPACE);
   expect("mmq null", int8_mixed_matmul_q(P, 64, 256, 16, nullptr, Pf, 128, P, P, 256, nullptr, nullptr),
          INT8MM_E_NULL);

@@ -136,6 +136,28 @@ def test_weight_only_rejects(L):
     assert wo(P, 4, 32, P, P, 32, UNALIGNED, None) == E_ALIGN
 
 
+@pytest.mark.parametrize("M,K,mo", [(64, 256, 16), (4096, 12288, 256), (17, 33024, 0),
+                                     (4097, 20480, 8192), (1, 16, 1)])
+def test_quant_state_layout(L, M, K, mo):
+    """The published offsets lie inside the state, 16-byte aligned, in disjoint ranges
+    that hold their fields (a_x, unit-tiled Xq, Xo, the column list, the count)."""
+    off = (ctypes.c_int64 * 6)()
+    assert L.int8_quant_state_layout(M, K, mo, off) == 0
+    total = L.int8_quant_state_bytes(M, K, mo)
+    o_stride = off[5]
+    assert o_stride % 16 == 0 and o_stride >= mo
+    rows, ks = (M + 15) // 16 * 16, (K + 63) // 64
+    spans = sorted([(off[0], 4 * M), (off[1], rows * ks * 64), (off[2], 2 * M * o_stride),
+                    (off[3], 4 * mo), (off[4], 4)])
+    for (a, n), (b, _) in zip(spans, spans[1:]):
+        assert a + n <= b
+    assert spans[-1][0] + spans[-1][1] <= total
+    assert all(off[i] % 16 == 0 for i in range(4)) and off[4] % 4 == 0
+    assert L.int8_quant_state_layout(M, K, mo, None) == E_NULL
+    assert L.int8_quant_state_layout(0, K, mo, off) == E_SHAPE
+    assert L.int8_quant_state_layout(M, K + 8, mo, off) == E_SHAPE
+
+
 def test_quantize_once_rejects_and_sizes(L):
     assert L.int8_quant_state_bytes(0, 64, 16) == 0
     assert L.int8_quant_state_bytes(4096, 12288, 256) > 4096 * 12288   # holds Xq
