@@ -10,7 +10,7 @@
 // output.
 //
 // One block per 16 RG output features (RG 16-row groups of the unit-tiled Wq; RG = 2
-// where N leaves more than 2048 blocks of 16, so that fewer blocks re-read X), 16 waves.
+// where N leaves more than 256 blocks of 16, so that fewer blocks re-read X), 16 waves.
 // Wave w takes k-steps w, w + 16, ... (64 columns each) in batches of kWoBatch; per
 // step every lane loads one 16-byte slice of the step's 1 KB weight unit and the two
 // 8-column pieces of X (its token, the same columns) that the MFMAs pair with it,
@@ -41,14 +41,33 @@ __device__ __forceinline__ v2u int8x4_to_half(unsigned d) {
   return o;
 }
 
-template <int RG>
+// XL: X staged once per block in LDS (rows of K halves, 16 bytes of padding between rows:
+// conflict-free fragment reads) by DMA, 1 KB per instruction straight from global memory,
+// instead of two 16-byte register loads per lane and step (half of them for tokens past
+// M): a third of the vector memory instructions. Needs K a multiple of 512 (whole 1 KB
+// row segments) and M x K x 2 <= kWoXLdsMax bytes.
+constexpr int kWoXLdsMax = 64 << 10;
+
+template <int RG, bool XL>
 __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a) {
   __shared__ float red[kWoWaves][16 * RG][17];
+  extern __shared__ __attribute__((aligned(16))) char xs[];  // XL: [M][2 K + 16]
   const int K = a.K, M = a.M, N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16 * RG;
   const int ks = unit_ks(K);
   const int g = lane >> 4, tok = lane & 15;
+  const int xstride = 2 * K + 16;
+  if constexpr (XL) {
+    // X rows into LDS: segment q of row m (1 KB) by one DMA instruction
+    const int segs = (2 * K) >> 10;
+    for (int t = wave; t < M * segs; t += kWoWaves) {
+      const int m = t / segs, q = t - m * segs;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const char*>(a.X) + static_cast<size_t>(m) * 2 * K + q * 1024 + 16 * lane,
+          (__attribute__((address_space(3))) void*)(xs + m * xstride + q * 1024), 16, 0, 0);
+    }
+  }
   const int8_t* wunit[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r)
@@ -69,15 +88,26 @@ __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a)
 #pragma unroll
       for (int r = 0; r < RG; ++r)
         wf[j][r] = *reinterpret_cast<const v4u*>(wunit[r] + static_cast<size_t>(s < ks ? s : 0) * kUnitBytes);
-      const unsigned o = s < ks ? x_off(s) : kOOB;
-      x0[j] = buf_load16(xr, o);
-      x1[j] = buf_load16(xr, o == kOOB ? kOOB : o + 16u);
+      if constexpr (!XL) {
+        const unsigned o = s < ks ? x_off(s) : kOOB;
+        x0[j] = buf_load16(xr, o);
+        x1[j] = buf_load16(xr, o == kOOB ? kOOB : o + 16u);
+      }
     }
   };
   load_batch(wave);
   // this thread's output (token m, feature n0 + nl) and its constant, loaded early
   const int m = tid / (16 * RG), nl = tid % (16 * RG), n = n0 + nl;
   const float aw_pre = a.a_w[min(n, N - 1)];
+  if constexpr (XL) {
+    // the DMA of every wave has landed (this thread's, then the barrier for the others';
+    // the weight loads issued after it may still be in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kWoBatch * RG + 1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  // tokens past M read row M - 1: their products land in discarded outputs
+  const char* xrow = xs + min(tok, M - 1) * xstride + 32 * g;
 
   v4f acc[RG];
 #pragma unroll
@@ -85,7 +115,12 @@ __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a)
   for (int base = wave;;) {
 #pragma unroll
     for (int j = 0; j < kWoBatch; ++j) {
-      if (base + kWoWaves * j < ks) {  // wave-uniform
+      const int s = base + kWoWaves * j;
+      if (s < ks) {  // wave-uniform
+        if constexpr (XL) {
+          x0[j] = *reinterpret_cast<const v4u*>(xrow + 128 * s);
+          x1[j] = *reinterpret_cast<const v4u*>(xrow + 128 * s + 16);
+        }
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
           const v2u h0 = int8x4_to_half(wf[j][r][0]), h1 = int8x4_to_half(wf[j][r][1]);
@@ -120,12 +155,20 @@ bool weight_only_supported(int64_t M, int64_t K) {
   return M >= 1 && M <= 16 && M * K * 2 < (int64_t(1) << 31);
 }
 
+// Measured per call (HIP graphs over rotated weights): 32 features per block pays from
+// 512 groups of 16 on (4 x 8192 x 8192: 14.8-15.0 against 16.2 us with 16 per block;
+// 8 x 4096 x 4096: 7.0 against 6.2 us); X staged in LDS pays with many tokens (16 x 2048
+// x 4096: 4.8 against 5.7 us) and costs its barrier with few (8 x 4096 x 4096: 6.45
+// against 6.2 us).
 hipError_t launch_weight_only(const WeightOnlyArgs& a, hipStream_t s) {
   const int nrg = a.N / 16;
-  if (nrg > 2048) {
-    hipLaunchKernelGGL(k_weight_only<2>, dim3((nrg + 1) / 2), dim3(64 * kWoWaves), 0, s, a);
+  if (nrg > 256) {
+    hipLaunchKernelGGL((k_weight_only<2, false>), dim3((nrg + 1) / 2), dim3(64 * kWoWaves), 0, s, a);
+  } else if (a.M >= 12 && a.K % 512 == 0 && static_cast<int64_t>(a.M) * a.K * 2 <= kWoXLdsMax) {
+    const size_t lds = static_cast<size_t>(a.M) * (2 * a.K + 16);
+    hipLaunchKernelGGL((k_weight_only<1, true>), dim3(nrg), dim3(64 * kWoWaves), lds, s, a);
   } else {
-    hipLaunchKernelGGL(k_weight_only<1>, dim3(nrg), dim3(64 * kWoWaves), 0, s, a);
+    hipLaunchKernelGGL((k_weight_only<1, false>), dim3(nrg), dim3(64 * kWoWaves), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -388,7 +388,9 @@ def test_graph_replay_matches_eager(M, K, N):
                                    (5, 12288, 64), (3, 16, 48), (16, 12288, 272),
                                    (7, 20480, 48), (12, 5136, 16),
                                    # 32 features per block, odd count of 16-feature groups
-                                   (3, 1040, 32784), (16, 528, 34816)])
+                                   (3, 1040, 32784), (16, 528, 34816), (4, 8192, 8192),
+                                   # X staged in LDS (M >= 12, K a multiple of 512)
+                                   (16, 2048, 4096), (12, 512, 80), (13, 2560, 528)])
 def test_weight_only_parity(M, K, N):
     """Weight-only int8 (no activation quantization) against the oracle's fp16(X @ W^)."""
     announce(f"weight-only M={M} K={K} N={N}")
