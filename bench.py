@@ -122,8 +122,15 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
     if copy_name is None:
         raise SystemExit("copy probe kernel not found; kernels seen: " + "; ".join(fetch))
     copy_kib = COPY_PROBE_BYTES / 1024.0
-    f_scale = copy_kib / (sum(fetch[copy_name]) / len(fetch[copy_name]))
-    w_scale = copy_kib / (sum(write[copy_name]) / len(write[copy_name]))
+
+    def probe_mean(vals):
+        # the probe's launches are the 1 GiB ones; the same elementwise kernel also runs on
+        # small buffers elsewhere in the run (the decode leg's copy floor)
+        big = [v for v in vals if v >= 0.5 * max(vals)]
+        return sum(big) / len(big)
+
+    f_scale = copy_kib / probe_mean(fetch[copy_name])
+    w_scale = copy_kib / probe_mean(write[copy_name])
     plans = {"k_gemm": (workload, None), "k_decode": ("decode_8x4096", None)}
     for kernel, (wl_name, _) in plans.items():
         names = [n for n in fetch if f"i8mm::{kernel}<" in n]
