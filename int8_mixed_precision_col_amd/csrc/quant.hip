@@ -627,6 +627,26 @@ __global__ __launch_bounds__(256) void k_quant_fix(FusedQuantArgs a, int o_lds, 
     before += i < wave ? wave_tot[i] : 0;
     count += wave_tot[i];
   }
+  // rows: patch (zero the provisional codes at every outlier column) when some column
+  // reaching the provisional constant is not an outlier, else requantize; decided as
+  // soon as the mask and the count are known, the ranking below alongside
+  const bool patch = count <= min(kFixZeroMax, o_lds);
+  bool redo[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = rbase + 4 * rr;
+    redo[rr] = row_block && row < a.M && !patch;
+    if (row_block && row < a.M && patch && count > 0 && ax[rr] > 0.0f) {
+      bool keep = false;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = js[rr][k];
+        keep = keep || (c >= 0 && !((g_s[c >> 5] >> (c & 31)) & 1u));
+      }
+      redo[rr] = !keep;
+    }
+    if (redo[rr] && lane == 0) redo_s[atomicAdd(&nredo_s, 1)] = row;
+  }
   for (int w = w0, r = before; w < w1; ++w) {
     uint32_t bits = g_s[w];
     while (bits) {
@@ -650,26 +670,6 @@ __global__ __launch_bounds__(256) void k_quant_fix(FusedQuantArgs a, int o_lds, 
   const _Float16* __restrict__ X = a.X;
 
   if (row_block) {
-    // rows: patch (zero the provisional codes at every outlier column) when some column
-    // reaching the provisional constant is not an outlier, else requantize
-    const bool patch = count <= min(kFixZeroMax, o_lds);
-    bool redo[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = rbase + 4 * rr;
-      redo[rr] = row < a.M && !patch;
-      if (row < a.M && patch && count > 0 && ax[rr] > 0.0f) {
-        bool keep = false;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = js[rr][k];
-          keep = keep || (c >= 0 && !((g_s[c >> 5] >> (c & 31)) & 1u));
-        }
-        redo[rr] = !keep;
-      }
-      if (redo[rr] && lane == 0) redo_s[atomicAdd(&nredo_s, 1)] = row;
-    }
-    lds_barrier();
     const int nredo = nredo_s;
     // the outlier values of the wave's rows (for up to 64 ranks, all four rows' loads
     // before any store: the pointers do not alias) and the zeroed codes
@@ -778,6 +778,7 @@ hipError_t launch_quant_fixup(const FusedQuantArgs& a, hipStream_t s) {
   else if (per <= 2) I8MM_QF(2);
   else if (per <= 4) I8MM_QF(4);
   else if (per <= 8) I8MM_QF(8);
+  else if (per <= 12) I8MM_QF(12);
   else I8MM_QF(16);
 #undef I8MM_QF
   return hipGetLastError();
