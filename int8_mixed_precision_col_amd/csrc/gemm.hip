@@ -98,14 +98,58 @@ hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
   return run_grouped<CfgS>(a, s, 8);
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (gemm_skinny_supported(g.M, g.N, g.K)) return launch_gemm_skinny(g, s);
-  const Tile t = pick_tile([&](int tn, int tm) {
-    return static_cast<long>((g.N + tn - 1) / tn) * ((g.M + tm - 1) / tm);
-  });
+// Features [n0, n1) of the product g as a product of its own (n0 a multiple of 16: the
+// slice starts at a unit-row boundary of Wq), writing into the same Y rows.
+static GemmArgs feature_slice(const GemmArgs& g, int n0, int n1) {
+  GemmArgs s = g;
+  s.Wq = g.Wq + static_cast<size_t>(n0 / kUnitRows) * unit_ks(g.K) * kUnitBytes;
+  s.a_w = g.a_w + n0;
+  if (g.WoT) s.WoT = g.WoT + static_cast<size_t>(n0) * g.o_stride;
+  s.Y = g.Y + n0;
+  if (g.acc_out) s.acc_out = g.acc_out + n0;
+  s.N = n1 - n0;
+  s.ldy = g.ldy > 0 ? g.ldy : g.N;
+  return s;
+}
+
+static hipError_t run_tile(Tile t, const GemmArgs& g, hipStream_t s) {
   if (t == Tile::L) return run<CfgL>(g, s, 8);
   if (t == Tile::M) return run<CfgM>(g, s, 8);
   return run<CfgS>(g, s, 8);
+}
+
+// Cost, in waves of 256 x 256 tiles, of the best single tile shape over M x N.
+static double best_cost(long M, long N, Tile* t) {
+  auto tiles = [&](int tn, int tm) { return ((N + tn - 1) / tn) * ((M + tm - 1) / tm); };
+  *t = pick_tile(tiles);
+  if (*t == Tile::L) return wave_cost(tiles(256, 256));
+  if (*t == Tile::M) return wave_cost(tiles(128, 256)) * (0.5 / 0.9);
+  return wave_cost(tiles(128, 128)) * (0.25 / 0.85);
+}
+
+// A last, partial wave of 256 x 256 tiles leaves CUs idle for a whole tile's time (the
+// 4096 x 20480 x 5120 product has 1.25 waves of them). When the output holds at least
+// one whole wave, the leading feature columns that fill whole waves take 256 x 256
+// tiles and the remaining features a second launch with the tile shape that suits
+// them, if the estimate (plus a twentieth of a wave for the second launch) is lower.
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (gemm_skinny_supported(g.M, g.N, g.K)) return launch_gemm_skinny(g, s);
+  Tile t1;
+  const double single = best_cost(g.M, g.N, &t1);
+  const long cus = device_cus(), tiles_m = (g.M + 255) / 256;
+  const long waves = static_cast<long>((g.N + 255) / 256) * tiles_m / cus;
+  const long n_split = waves * cus / tiles_m * 256;
+  if (waves >= 1 && n_split > 0 && n_split < g.N) {
+    Tile t2;
+    const double rest = best_cost(g.M, g.N - n_split, &t2);
+    const double lead = wave_cost(n_split / 256 * tiles_m);
+    if (lead + rest + 0.05 < single) {
+      const hipError_t e = run<CfgL>(feature_slice(g, 0, int(n_split)), s, 8);
+      if (e != hipSuccess) return e;
+      return run_tile(t2, feature_slice(g, int(n_split), g.N), s);
+    }
+  }
+  return run_tile(t1, g, s);
 }
 
 }  // namespace i8mm

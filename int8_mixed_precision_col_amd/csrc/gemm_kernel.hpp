@@ -179,6 +179,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   const int o_pad = min((count + 15) & ~15, g.o_stride);
   const int nvalid = min(count, g.max_outliers);
   const int M = g.M, N = g.N, ks = unit_ks(g.K);
+  const size_t ldy = g.ldy > 0 ? g.ldy : N;
   auto stage_outliers = [&](int s0) {
     for (int t = tid; t < (C::TN + C::TM) * 2; t += C::NT) {
       const int row = t >> 1, h = t & 1;
@@ -220,7 +221,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
         if (g.acc_out && m < M && n0 + nq < N) {
           const v4i av = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]};
-          *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(m) * N + n0 + nq) = av;
+          *reinterpret_cast<v4i*>(g.acc_out + m * ldy + n0 + nq) = av;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[4 * q + e] = static_cast<float>(acc[i][j][4 * q + e]) * sx * aw[e];
@@ -281,7 +282,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
     const int r = t * RPI + lane / CH;
     const v4u v = *reinterpret_cast<const v4u*>(ys + r * RB + 16 * (c ^ ysw<CH>(r)));
     const int m = m0 + wm * C::WTM + r;
-    if (m < M && n < N) *reinterpret_cast<v4u*>(g.Y + static_cast<size_t>(m) * N + n) = v;
+    if (m < M && n < N) *reinterpret_cast<v4u*>(g.Y + m * ldy + n) = v;
   }
 }
 

@@ -94,8 +94,9 @@ struct GemmArgs {
   int o_stride;
   const int32_t* count;
   int max_outliers;
-  _Float16* Y;          // [M][N]
-  int32_t* acc_out;     // nullable [M][N]
+  _Float16* Y;          // [M][ldy]
+  int32_t* acc_out;     // nullable [M][ldy]
+  int ldy;              // row stride of Y and acc_out in elements (0: N)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // A handful of tokens: the weight-stream form of the same product (one block per 16

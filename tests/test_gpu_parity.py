@@ -183,6 +183,9 @@ CASES = [
     # prefill, weight-stream GEMM for a few tokens (token groups x feature groups per
     # block: 1x1, 2x1, 3x1, 4x1, 2x2)
     (9, 8208, 272), (24, 4096, 1040), (40, 2064, 1040), (64, 1024, 2064), (20, 1040, 32784),
+    # prefill, two launches: the features that fill whole waves of 256 x 256 tiles, then
+    # the remaining features on 128 x 128 tiles writing into the same output rows
+    (4096, 1024, 4352), (4000, 1040, 4400),
 ]
 
 
@@ -405,7 +408,7 @@ def test_weight_only_parity(M, K, N):
 
 @pytest.mark.parametrize("M,K,Ns", [(300, 1040, (528, 272, 1040)), (8, 4096, (1024, 512)),
                                     (64, 8192, (256,)), (5, 1024, (32784, 65552)),
-                                    (129, 1040, (16608,))])
+                                    (129, 1040, (16608,)), (4000, 528, (4400,))])
 def test_quantize_once_feeds_several_weights(M, K, Ns):
     """One activation quantization, several weights: each product equals the oracle
     (acc bit-exact, Y within tolerance) and, on the multi-kernel path, the one-call
