@@ -11,11 +11,14 @@
 //                   int8 weight dequantized, fp16(Wq a_w / 127))
 //
 // gfx950 design. Both operands are K-contiguous, so a block computes D = Wq_tile *
-// Xq_tile^T with v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with 16 consecutive K
-// bytes of each operand, and the A/B roles are chosen so that every lane ends up
-// holding 4 consecutive output columns n of one row m (8-byte fp16 stores).
+// Xq_tile^T with v_mfma_i32_16x16x64_i8: lane l feeds row l%16 with 16 consecutive K
+// bytes (chunk l/16 of a 64-byte slab row) of each operand, and the A/B roles are
+// chosen so that every lane ends up holding 4 consecutive output columns n of one row
+// m (8-byte fp16 stores). Under the board's power limit the 16x16x64 form sustains
+// more int8 operations per second than 32x32x32 on the same operands: it moves half
+// the accumulator bits per operation.
 // A block of WGN x WGM waves owns a TN x TM tile; each wave a (TN/WGN) x (TM/WGM)
-// sub-tile of 32x32 blocks whose int32 accumulators live in registers.
+// sub-tile of 16x16 blocks whose int32 accumulators live in registers.
 // K is walked in BK-byte slabs through a ring of STAGES LDS buffers filled by
 // global_load_lds_dwordx4 (global memory straight into LDS, no VGPR staging) from
 // unit-tiled operands (16 rows x 64 K-bytes per contiguous 1 KB unit), so that each
@@ -25,7 +28,7 @@
 // belongs at its LDS slot under an XOR swizzle, so that the ds_read_b128 fragment
 // reads are free of bank conflicts. Slab kt + STAGES - 1 is in
 // flight while slab kt is multiplied; one barrier per slab.
-// The outlier product runs after the K loop on v_mfma_f32_32x32x16_f16, with the
+// The outlier product runs after the K loop on v_mfma_f32_16x16x16_f16, with the
 // small Xo / W^ fragments staged through LDS (W^ gathered beforehand, or dequantized
 // from the Wq bytes of the outlier columns as they are staged), accumulating on top of
 // the already
@@ -45,19 +48,19 @@ struct GemmCfg {
   static constexpr int CPOL = CPOL_;
   static constexpr int NW = WGN * WGM, NT = NW * 64;
   static constexpr int WTN = TN / WGN, WTM = TM / WGM;
-  static constexpr int BN = WTN / 32, BM = WTM / 32;
+  static constexpr int BN = WTN / 16, BM = WTM / 16;
   static constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
   static constexpr int A_BYTES = TN * BK, B_BYTES = TM * BK;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int AI = A_BYTES / (1024 * NW);    // 1 KB DMA instructions per wave, A
   static constexpr int BI = B_BYTES / (1024 * NW);    // ... and B
   static_assert(AI * 1024 * NW == A_BYTES && BI * 1024 * NW == B_BYTES, "tile / wave mismatch");
-  static_assert(BK % 64 == 0 && WTN % 32 == 0 && WTM % 32 == 0, "shape");
+  static_assert(BK == 64 && WTN % 32 == 0 && WTM % 32 == 0, "shape");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
 };
 
 // XOR swizzle of the 16-byte chunk index within an LDS row. For the fragment reads
-// (lanes 0..31 read rows r0..r0+31 at one chunk, lanes 32..63 the next chunk) every
+// (lanes 16c .. 16c + 15 read rows r0 .. r0 + 15, r0 a multiple of 16, at chunk c) every
 // group of 8 lanes hits 8 distinct 16-byte slots of a 128-byte window and every group
 // of 16 lanes 16 distinct slots of a 256-byte window.
 template <int CPR>
@@ -145,8 +148,8 @@ __device__ __forceinline__ char* wave_slice(int w) {
     if (st == 2) return stage_buf<C, 2>() + off;
   return (st == 1 ? stage_buf<C, 1>() : stage_buf<C, 0>()) + off;
 }
-// Chunk swizzle of a staged output row: spreads the 32 rows written by one fragment store
-// (one 16-byte chunk each) over 16 distinct bank groups.
+// Chunk swizzle of a staged output row: spreads the 16 rows written by one fragment store
+// (half of a 16-byte chunk each, two lanes per chunk) over 16 distinct bank groups.
 template <int CH>
 __device__ __forceinline__ int ysw(int r) {
   static_assert(CH == 16 || CH == 8, "staged row width");
@@ -154,16 +157,16 @@ __device__ __forceinline__ int ysw(int r) {
   else return (r >> 1) & 7;
 }
 
-// Epilogue. 32x32 accumulator layout: lane l, register r holds column m = l % 32 and
-// row n = 8 (r / 4) + 4 (l / 32) + r % 4 of the block (rows are n here). The tile's
+// Epilogue. 16x16 accumulator layout: lane l, register r holds column m = l % 16 and
+// row n = 4 (l / 16) + r of the block (rows are n here). The tile's
 // a_w / a_x and the outlier fragments (16 columns of W^ and Xo per pass) are staged
 // in stage 0 of the ring first (free once the K loop is done), so that no global
 // load waits inside the per-block loops; reading them straight from global memory,
-// one block of 32 x 32 at a time, took ~13 us per tile against ~8 us now. Per block:
+// one block at a time, took ~13 us per tile against ~8 us now. Per block:
 // store the int32 sums if asked, dequantize in place to fp32, let the fp16 outlier
 // MFMA accumulate on top of that, round once to fp16.
 template <class C, bool GATHER>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::BN][C::BM],
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v4i (&acc)[C::BN][C::BM],
                                                      int n0, int m0, int wn, int wm, int lane,
                                                      int tid) {
   constexpr int OS = 24;  // staged row stride in halves (16 columns + 8 of padding)
@@ -173,7 +176,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   float* ax_s = aw_s + C::TN;
   _Float16* wo_s = reinterpret_cast<_Float16*>(ax_s + C::TM);
   _Float16* xo_s = wo_s + C::TN * OS;
-  const int l32 = lane & 31, lhi = lane >> 5;
+  const int l16 = lane & 15, lq = lane >> 4;
   const int count = *g.count;
   const bool overflow = count > g.max_outliers;
   const int o_pad = min((count + 15) & ~15, g.o_stride);
@@ -207,26 +210,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < C::BN; ++i) {
-    const int nl = wn * C::WTN + i * 32;
+    const int nl = wn * C::WTN + i * 16;
+    const int nq = nl + 4 * lq;
+    const v4f aw = *reinterpret_cast<const v4f*>(aw_s + nq);
 #pragma unroll
     for (int j = 0; j < C::BM; ++j) {
-      const int ml = wm * C::WTM + j * 32;
-      const int m = m0 + ml + l32;
-      const float sx = ax_s[ml + l32] * kInvQMax2;
-      v16f y;
+      const int ml = wm * C::WTM + j * 16;
+      const int m = m0 + ml + l16;
+      const float sx = ax_s[ml + l16] * kInvQMax2;
+      if (g.acc_out && m < M && n0 + nq < N)
+        *reinterpret_cast<v4i*>(g.acc_out + m * ldy + n0 + nq) = acc[i][j];
+      v4f y;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nq = nl + 8 * q + 4 * lhi;
-        const v4f aw = *reinterpret_cast<const v4f*>(aw_s + nq);
-        if (g.acc_out && m < M && n0 + nq < N) {
-          const v4i av = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]};
-          *reinterpret_cast<v4i*>(g.acc_out + m * ldy + n0 + nq) = av;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[4 * q + e] = static_cast<float>(acc[i][j][4 * q + e]) * sx * aw[e];
-      }
-      acc[i][j] = __builtin_bit_cast(v16i, y);
+      for (int e = 0; e < 4; ++e) y[e] = static_cast<float>(acc[i][j][e]) * sx * aw[e];
+      acc[i][j] = __builtin_bit_cast(v4i, y);
     }
   }
   for (int s0 = 0; s0 < o_pad; s0 += 16) {
@@ -237,14 +234,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
     }
 #pragma unroll
     for (int i = 0; i < C::BN; ++i) {
-      const int nl = wn * C::WTN + i * 32;
+      const int nl = wn * C::WTN + i * 16;
 #pragma unroll
       for (int j = 0; j < C::BM; ++j) {
-        const int ml = wm * C::WTM + j * 32;
-        const v8h fa = *reinterpret_cast<const v8h*>(wo_s + (nl + l32) * OS + 8 * lhi);
-        const v8h fb = *reinterpret_cast<const v8h*>(xo_s + (ml + l32) * OS + 8 * lhi);
-        acc[i][j] = __builtin_bit_cast(v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                                 fa, fb, __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
+        const int ml = wm * C::WTM + j * 16;
+        const v4h fa = *reinterpret_cast<const v4h*>(wo_s + (nl + l16) * OS + 4 * lq);
+        const v4h fb = *reinterpret_cast<const v4h*>(xo_s + (ml + l16) * OS + 4 * lq);
+        acc[i][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_mfma_f32_16x16x16f16(
+                                                fa, fb, __builtin_bit_cast(v4f, acc[i][j]), 0, 0, 0));
       }
     }
   }
@@ -261,17 +258,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, v16i (&acc)[C::
   for (int i = 0; i < C::BN; ++i) {
 #pragma unroll
     for (int j = 0; j < C::BM; ++j) {
-      const int r = j * 32 + l32;
-      const v16f y = __builtin_bit_cast(v16f, acc[i][j]);
+      const int r = j * 16 + l16;
+      const v4f y = __builtin_bit_cast(v4f, acc[i][j]);
+      v4h out;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v4h out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          out[e] = overflow ? static_cast<_Float16>(__builtin_nanf(""))
-                            : static_cast<_Float16>(y[4 * q + e]);
-        *reinterpret_cast<v4h*>(ys + r * RB + 16 * ((4 * i + q) ^ ysw<CH>(r)) + 8 * lhi) = out;
-      }
+      for (int e = 0; e < 4; ++e)
+        out[e] = overflow ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y[e]);
+      *reinterpret_cast<v4h*>(ys + r * RB + 16 * ((2 * i + (lane >> 5)) ^ ysw<CH>(r)) +
+                              8 * (lq & 1)) = out;
     }
   }
   constexpr int RPI = 64 / CH;     // rows per store instruction
@@ -294,7 +288,7 @@ struct GemmBlock {
   int a_k[C::AI], b_k[C::BI];   // K offset of this lane's chunk within a slab
   int wave, lane, wn, wm;
   int rn0, rm0;   // first fragment row of this lane in the A / B tile
-  v16i acc[C::BN][C::BM];
+  v4i acc[C::BN][C::BM];
 
   // Issue the DMA of slab kt into stage S (one 1 KB LDS block per instruction).
   // Slab kt starts kt * BK / 64 units further along each row group.
@@ -337,18 +331,18 @@ struct GemmBlock {
     v4i a[C::BN], b[C::BM];
   };
 
-  // Fragments of substep s (32 K bytes) of the slab held in stage S.
+  // Fragments of the slab held in stage S: chunk l / 16 of rows l % 16 of each block.
   template <int S>
-  __device__ __forceinline__ void load_frags(Frags& f, int s) const {
+  __device__ __forceinline__ void load_frags(Frags& f) const {
     const char* As = stage_buf<C, S>();
     const char* Bs = As + C::A_BYTES;
-    const int c = 2 * s + (lane >> 5);
+    const int c = lane >> 4;
 #pragma unroll
     for (int i = 0; i < C::BN; ++i)
-      f.a[i] = *reinterpret_cast<const v4i*>(As + lds_off<C::BK>(rn0 + i * 32, c));
+      f.a[i] = *reinterpret_cast<const v4i*>(As + lds_off<C::BK>(rn0 + i * 16, c));
 #pragma unroll
     for (int j = 0; j < C::BM; ++j)
-      f.b[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 32, c));
+      f.b[j] = *reinterpret_cast<const v4i*>(Bs + lds_off<C::BK>(rm0 + j * 16, c));
   }
 
   // The MFMAs of one substep with the DMA of slab kt into stage S spread between them:
@@ -362,7 +356,7 @@ struct GemmBlock {
     for (int i = 0; i < C::BN; ++i)
 #pragma unroll
       for (int j = 0; j < C::BM; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
         if ((i * C::BM + j) % EVERY == EVERY - 1 && (i * C::BM + j) / EVERY < NQ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_one<S>(kt, (i * C::BM + j) / EVERY);
@@ -373,42 +367,19 @@ struct GemmBlock {
     for (int q = NMM / EVERY; q < NQ; ++q) issue_one<S>(kt, q);
   }
 
-  __device__ __forceinline__ void mma(const Frags& f) {
-#pragma unroll
-    for (int i = 0; i < C::BN; ++i)
-#pragma unroll
-      for (int j = 0; j < C::BM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-  }
-
-  // One K slab held in stage CUR, whose first-substep fragments are already in f.
-  // Substep s + 1's fragments are read while substep s multiplies. Before the last
-  // substep (whose fragments are in registers by then): wait until slab kt + 1 has
-  // landed (this thread's DMA, then the barrier for everyone else's; the slabs up to
-  // kt + STAGES - 1 may still be in flight), read slab kt + 1's first fragments, and
-  // run the last MFMAs of slab kt with the refill of stage CUR - free now that every
+  // One K slab held in stage CUR, whose fragments are already in f: wait until slab
+  // kt + 1 has landed (this thread's DMA, then the barrier for everyone else's; the
+  // slabs up to kt + STAGES - 1 may still be in flight), read slab kt + 1's fragments,
+  // and run the MFMAs of slab kt with the refill of stage CUR - free now that every
   // wave has read all of slab kt - by slab kt + STAGES spread between them.
+  // sched_barrier(0) keeps the compiler from sinking the fragment reads down to their
+  // MFMAs, which would expose the LDS latency once per slab.
   template <int CUR>
   __device__ __forceinline__ void step(int kt, Frags& f) {
-    constexpr int S = C::STAGES, NS = C::BK / 32;
+    constexpr int S = C::STAGES;
     Frags nxt;
-    // sched_barrier(0) keeps the compiler from sinking the fragment reads down to
-    // their MFMAs, which would expose the LDS latency once per substep. The explicit
-    // LDS-read drain before each read batch (whose targets were read a whole MFMA
-    // block earlier, so it costs nothing) lets the MFMAs run without a wait: with DMA
-    // in flight the compiler would otherwise wait for every LDS read, the batch just
-    // issued included, before the first MFMA.
-#pragma unroll
-    for (int s = 0; s + 1 < NS; ++s) {
-      lds_reads_done();
-      load_frags<CUR>(nxt, s + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f);
-      __builtin_amdgcn_sched_barrier(0);
-      f = nxt;
-    }
     wait_and_barrier<(S - 2) * (C::AI + C::BI)>();
-    load_frags<(CUR + 1) % S>(nxt, 0);
+    load_frags<(CUR + 1) % S>(nxt);
     __builtin_amdgcn_sched_barrier(0);
     mma_dma<CUR>(f, kt + S);
     __builtin_amdgcn_sched_barrier(0);
@@ -432,8 +403,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
     // in as a scalar they hide which LDS stage a read touches, and the compiler then
     // waits for every outstanding DMA before each fragment read.
     const int vw = tid >> 6;
-    b.rn0 = (vw % C::WGN) * C::WTN + (b.lane & 31);
-    b.rm0 = (vw / C::WGN) * C::WTM + (b.lane & 31);
+    b.rn0 = (vw % C::WGN) * C::WTN + (b.lane & 15);
+    b.rm0 = (vw / C::WGN) * C::WTM + (b.lane & 15);
   }
   const int n0 = tn * C::TN, m0 = tm * C::TM;
   const int K = g.K;
@@ -461,7 +432,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
 #pragma unroll
   for (int i = 0; i < C::BN; ++i)
 #pragma unroll
-    for (int j = 0; j < C::BM; ++j) b.acc[i][j] = v16i{};
+    for (int j = 0; j < C::BM; ++j) b.acc[i][j] = v4i{};
 
   // K slabs, padded to a multiple of STAGES: the padding slabs read as zeros and add
   // nothing to the exact int32 sums.
@@ -473,7 +444,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tn, int tm) {
   if constexpr (C::STAGES >= 4) b.template issue<3>(3);
   typename GemmBlock<C>::Frags f;
   wait_and_barrier<(C::STAGES - 1) * (C::AI + C::BI)>();   // slab 0 landed
-  b.template load_frags<0>(f, 0);
+  b.template load_frags<0>(f);
   for (int kt = 0; kt < nk_pad; kt += C::STAGES) {
     b.template step<0>(kt, f);
     b.template step<1>(kt + 1, f);
