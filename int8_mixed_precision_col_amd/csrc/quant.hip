@@ -384,8 +384,10 @@ void quant_fused_geometry(int64_t M, int64_t K, int* rows_per_block, int* nblk) 
 
 constexpr int kListSlot = 4 + kFlagListCap;  // ints per published list: count, 3 pad, columns
 
-// Block b: rows [b * rows_per_block, ...), each held by the whole block (thread t takes
-// chunks t + 256 i), the next row's loads in flight while the current one is processed.
+// Block b: rows b, b + nblk, b + 2 nblk, ... (at most rows_per_block of them), each held
+// by the whole block (thread t takes chunks t + 256 i), the next row's loads in flight
+// while the current one is processed. Interleaved rather than consecutive rows: the
+// blocks' first loads then cover one contiguous stretch of X (13B down pass: 62 -> 58 us).
 template <int CH>
 __global__ __launch_bounds__(256) void k_quant_pass(FusedQuantArgs a) {
   extern __shared__ uint32_t mask_s[];  // the block's column flags, ceil(K / 32) words
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(256) void k_quant_pass(FusedQuantArgs a) {
   if (blockIdx.x == 0)
     for (int w = tid; w < W; w += 256) a.gmask[w] = 0u;
   lds_barrier();
-  const int r0 = blockIdx.x * a.rows_per_block, r1 = min(a.M, r0 + a.rows_per_block);
+  const int S = a.nblk, first = blockIdx.x, last = first + (a.M - 1 - first) / S * S;
 
   auto process = [&](v8h (&v)[CH], int row, int par) {
     // flags |x| >= t (rare: their halves are cleared and ORed into the block mask) and
@@ -472,15 +474,15 @@ __global__ __launch_bounds__(256) void k_quant_pass(FusedQuantArgs a) {
 
   // The next row's loads are always issued (past the block's last row they re-read it):
   // loads under a condition make the compiler wait for them where the paths join.
-  if (r0 < r1) {
+  {
     v8h A[CH], B[CH];
-    load_row<CH, 256>(a.X + static_cast<size_t>(r0) * K, K, tid, A);
-    for (int row = r0; row < r1; row += 2) {
-      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + 1, r1 - 1)) * K, K, tid, B);
+    load_row<CH, 256>(a.X + static_cast<size_t>(first) * K, K, tid, A);
+    for (int row = first; row <= last; row += 2 * S) {
+      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + S, last)) * K, K, tid, B);
       process(A, row, 0);
-      if (row + 1 >= r1) break;
-      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + 2, r1 - 1)) * K, K, tid, A);
-      process(B, row + 1, 1);
+      if (row + S > last) break;
+      load_row<CH, 256>(a.X + static_cast<size_t>(min(row + 2 * S, last)) * K, K, tid, A);
+      process(B, row + S, 1);
     }
   }
 
