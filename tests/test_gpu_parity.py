@@ -32,7 +32,9 @@ def weight(seed, K, N, std=0.02):
 # ------------------------------------------------------------------ prepare
 
 @pytest.mark.parametrize("K,N,layout", [(1024, 1024, 0), (1040, 528, 0), (1040, 528, 1),
-                                        (16, 16, 0), (4112, 80, 1), (48, 32, 0), (48, 32, 1)])
+                                        (16, 16, 0), (4112, 80, 1), (48, 32, 0), (48, 32, 1),
+                                        # wide [K, N] weights, ragged in K and N
+                                        (1040, 49216, 0), (2064, 24528, 0)])
 def test_prepare_weight_bit_exact(K, N, layout):
     announce(f"prepare_weight K={K} N={N} layout={layout}")
     W = weight(K + N, K, N)
