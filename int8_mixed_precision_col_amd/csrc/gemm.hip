@@ -7,16 +7,16 @@ namespace i8mm {
 using CfgL = GemmCfg<256, 256, 64, 2, 4, 4>;
 // 128 features x 256 tokens, 8 waves (64 x 64 each), 4-stage ring (96 KB).
 using CfgM = GemmCfg<128, 256, 64, 2, 4, 4>;
-// 128 x 128 tiles, 4 waves, 3-stage ring.
-using CfgS = GemmCfg<128, 128, 64, 2, 2, 3>;
+// 128 x 128 tiles, 8 waves (64 x 32 each), 4-stage ring (64 KB).
+using CfgS = GemmCfg<128, 128, 64, 2, 4, 4>;
 
 // Which tile shape: the one with the least estimated time, counted in waves of tiles
 // over the CUs times the tile's cost relative to a 256 x 256 tile (its area over its
 // measured rate: 1, 0.9 and 0.85 of the 256 x 256 rate on full waves). A last, partial
 // wave of tiles costs at least 0.6 of a full one: its tiles run alone but not faster
-// in proportion. On MI355X this picks the measured fastest shape for 2048 x 4096 x
-// {4096, 12288, 16384}, 4096 x 20480 x 5120, 4096 x 12288 x 49152, 1024 x 4096 x 4096 and
-// 512 x 8192 x 8192.
+// in proportion. On MI355X this picks the measured fastest shape, or one within 3% of
+// it, for 2048 x 4096 x {4096, 12288, 16384}, 4096 x 4096 x 4096, 4096 x 20480 x 5120,
+// 4096 x 12288 x 49152, 1024 x 4096 x 4096 and 512 x 8192 x 8192.
 enum class Tile { L, M, S };
 static int device_cus() {
   static int cus = 0;
