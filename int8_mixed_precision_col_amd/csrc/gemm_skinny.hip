@@ -14,11 +14,10 @@
 // 1 KB unit is exactly one 16 x 64 operand of v_mfma_i32_16x16x64_i8), in batches of
 // kSkBatch steps, double-buffered in registers so that the next batch is in flight
 // while this one multiplies. The waves' int32 partials are summed exactly through LDS.
-// The epilogue is k_gemm's: per 32 x 32 block of (feature, token), dequantize in fp32
-// as acc * (a_x * 1/127^2) * a_w, add the outlier product with v_mfma_f32_32x32x16_f16
+// The epilogue is k_gemm's: per 16 x 16 block of (feature, token), dequantize in fp32
+// as acc * (a_x * 1/127^2) * a_w, add the outlier product with v_mfma_f32_16x16x16_f16
 // over the same 16-column chunks of Xo and the dequantized outlier weights in the same
-// order, round once to fp16;
-// so Y is bit-identical to k_gemm's for the same inputs.
+// order, round once to fp16; so Y is bit-identical to k_gemm's for the same inputs.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -44,13 +43,12 @@ __device__ __attribute__((aligned(16))) const int kSkZero[4] = {0, 0, 0, 0};
 template <int G, int RG>
 __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
   constexpr int NR = 16 * RG, NM = 16 * G;                   // features, tokens per block
-  constexpr int EN = (NR + 31) / 32, EM = (NM + 31) / 32;    // 32 x 32 epilogue blocks
   constexpr int OS = 24;   // staged row stride in halves (16 columns + 8 of padding)
   __shared__ int red[kSkWaves][RG * G * 256];
   __shared__ int sum_s[RG * G * 256];
-  __shared__ float aw_s[32 * EN], ax_s[32 * EM];
-  __shared__ __attribute__((aligned(16))) _Float16 wo_s[32 * EN * OS];
-  __shared__ __attribute__((aligned(16))) _Float16 xo_s[32 * EM * OS];
+  __shared__ float aw_s[NR], ax_s[NM];
+  __shared__ __attribute__((aligned(16))) _Float16 wo_s[NR * OS];
+  __shared__ __attribute__((aligned(16))) _Float16 xo_s[NM * OS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,20 +126,20 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
   const bool overflow = count > g.max_outliers;
   const int o_pad = min((count + 15) & ~15, g.o_stride);
   const int nvalid = min(count, g.max_outliers);
-  for (int t = tid; t < 32 * EN; t += kSkThreads) aw_s[t] = g.a_w[min(n0 + t, N - 1)];
-  for (int t = tid; t < 32 * EM; t += kSkThreads) ax_s[t] = g.a_x[min(t, M - 1)];
+  for (int t = tid; t < NR; t += kSkThreads) aw_s[t] = g.a_w[min(n0 + t, N - 1)];
+  for (int t = tid; t < NM; t += kSkThreads) ax_s[t] = g.a_x[min(t, M - 1)];
   // the outlier columns s0 .. s0 + 15: the block's weight rows (gathered beforehand, or
   // dequantized from Wq) and Xo
   auto stage_outliers = [&](int s0) {
-    for (int t = tid; t < 32 * (EN + EM) * 2; t += kSkThreads) {
+    for (int t = tid; t < (NR + NM) * 2; t += kSkThreads) {
       const int row = t >> 1, h = t & 1;
-      if (row < 32 * EN)
+      if (row < NR)
         *reinterpret_cast<v8h*>(wo_s + row * OS + 8 * h) =
             g.WoT ? *reinterpret_cast<const v8h*>(g.WoT + static_cast<size_t>(min(n0 + row, N - 1)) * g.o_stride + s0 + 8 * h)
                   : outlier_weights(g, min(n0 + row, N - 1), s0 + 8 * h, nvalid, ks);
       else
-        *reinterpret_cast<v8h*>(xo_s + (row - 32 * EN) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
-            g.Xo + static_cast<size_t>(min(row - 32 * EN, M - 1)) * g.o_stride + s0 + 8 * h);
+        *reinterpret_cast<v8h*>(xo_s + (row - NR) * OS + 8 * h) = *reinterpret_cast<const v8h*>(
+            g.Xo + static_cast<size_t>(min(row - NR, M - 1)) * g.o_stride + s0 + 8 * h);
     }
   };
   if (o_pad > 0) stage_outliers(0);
@@ -154,39 +152,25 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
   }
   __syncthreads();
 
-  // epilogue: wave e < EN EM takes the 32 x 32 block (features 32 (e / EM) .., tokens
-  // 32 (e % EM) ..); 32x32 layout: lane l, register v -> token l % 32, feature
-  // 8 (v / 4) + 4 (l / 32) + v % 4
-  const bool ep = wave < EN * EM;
-  const int en = ep ? wave / EM : 0, em = ep ? wave % EM : 0;
-  const int l32 = lane & 31, lhi = lane >> 5;
-  const int mloc = 32 * em + l32;
-  v16f y;
+  // epilogue: wave e < RG G takes the 16 x 16 block (features 16 (e / G) .., tokens
+  // 16 (e % G) ..); 16x16 layout: lane l, register v -> token l % 16, feature
+  // 4 (l / 16) + v
+  const bool ep = wave < RG * G;
+  const int en = ep ? wave / G : 0, em = ep ? wave % G : 0;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int mloc = 16 * em + l16, nloc = 16 * en + 4 * lq, n = n0 + nloc;
+  v4f y;
   if (ep) {
     const float sx = ax_s[mloc] * kInvQMax2;
+    const int* blk = sum_s + (en * G + em) * 256 + (4 * lq) * 16 + l16;
+    v4i av;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int nloc = 32 * en + 8 * (v >> 2) + 4 * lhi + (v & 3);
-      const int a = nloc < NR && mloc < NM
-                        ? sum_s[((nloc >> 4) * G + (mloc >> 4)) * 256 + (nloc & 15) * 16 + (mloc & 15)]
-                        : 0;
-      y[v] = static_cast<float>(a) * sx * aw_s[nloc];
+    for (int v = 0; v < 4; ++v) {
+      av[v] = blk[16 * v];
+      y[v] = static_cast<float>(av[v]) * sx * aw_s[nloc + v];
     }
-    if (g.acc_out && mloc < M) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nloc = 32 * en + 8 * q + 4 * lhi, n = n0 + nloc;
-        if (nloc < NR && n < N) {
-          v4i av;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int nl = nloc + e;
-            av[e] = sum_s[((nl >> 4) * G + (mloc >> 4)) * 256 + (nl & 15) * 16 + (mloc & 15)];
-          }
-          *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(mloc) * N + n) = av;
-        }
-      }
-    }
+    if (g.acc_out && mloc < M && n < N)
+      *reinterpret_cast<v4i*>(g.acc_out + static_cast<size_t>(mloc) * N + n) = av;
   }
   for (int s0 = 0; s0 < o_pad; s0 += 16) {  // block-uniform trip count
     if (s0 > 0) {
@@ -195,23 +179,17 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
       __syncthreads();
     }
     if (ep) {
-      const v8h fa = *reinterpret_cast<const v8h*>(wo_s + (32 * en + l32) * OS + 8 * lhi);
-      const v8h fb = *reinterpret_cast<const v8h*>(xo_s + (32 * em + l32) * OS + 8 * lhi);
-      y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
+      const v4h fa = *reinterpret_cast<const v4h*>(wo_s + (16 * en + l16) * OS + 4 * lq);
+      const v4h fb = *reinterpret_cast<const v4h*>(xo_s + (16 * em + l16) * OS + 4 * lq);
+      y = __builtin_amdgcn_mfma_f32_16x16x16f16(fa, fb, y, 0, 0, 0);
     }
   }
-  if (ep && mloc < M) {
+  if (ep && mloc < M && n < N) {
+    v4h out;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nloc = 32 * en + 8 * q + 4 * lhi, n = n0 + nloc;
-      if (nloc < NR && n < N) {
-        v4h out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          out[e] = overflow ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y[4 * q + e]);
-        *reinterpret_cast<v4h*>(g.Y + static_cast<size_t>(mloc) * N + n) = out;
-      }
-    }
+    for (int e = 0; e < 4; ++e)
+      out[e] = overflow ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y[e]);
+    *reinterpret_cast<v4h*>(g.Y + static_cast<size_t>(mloc) * N + n) = out;
   }
 }
 
