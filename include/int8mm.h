@@ -275,16 +275,18 @@ const char* int8mm_strerror(int code);
 
 /*
  * Optional event timing, for benchmarks. int8mm_timing_enable(mode): 0 off; 1: each call
- * records a HIP event pair on its stream around its main kernel (the MFMA GEMM, the
- * decode kernel or the weight-only kernel); 2: also around the two activation
- * quantization kernels. Other modes are INT8MM_E_SHAPE. Not for calls under graph
+ * records a HIP event pair on its stream around its main kernels (the MFMA GEMM: one
+ * launch, or two when a partial last wave of 256 x 256 tiles is split off; the decode
+ * kernel; the weight-only kernel); 2: also around each of the two activation
+ * quantization phases. Other modes are INT8MM_E_SHAPE. Not for calls under graph
  * capture (the events would be captured). int8mm_timing_read_phases synchronises on the
- * recorded events and returns, per phase, the summed milliseconds and launch counts
- * since the last read: phase 0 is the pass over X (flags, provisional row constants and
- * codes; for K > 32768 the outlier-mask kernel), phase 1 the fix-up (outlier list, the
- * rows it changes, outlier gathers; for K > 32768 the row-quantization kernel), phase 2
- * the main kernel. It then starts a
- * new period; int8mm_timing_read does the same and returns phase 2 only. Not thread-safe.
+ * recorded events and returns, per phase, the summed milliseconds and the number of
+ * bracketed calls since the last read: phase 0 is the pass over X (flags, provisional
+ * row constants and codes; for K > 32768 the outlier-mask kernel), phase 1 the fix-up
+ * (two launches: the outlier column set, then the rows it changes and the outlier
+ * gathers; for K > 32768 the row-quantization kernel), phase 2 the main kernels. It then
+ * starts a new period; int8mm_timing_read does the same and returns phase 2 only. Not
+ * thread-safe.
  */
 int int8mm_timing_enable(int mode);
 int int8mm_timing_read(double* total_ms, int64_t* launches);
