@@ -192,9 +192,9 @@ def prepare(binding, torch, wl, inputs, copies: int, time_prepare: bool = False)
 
 def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y, mode: int = 1):
     """n_calls int8_mixed_matmul calls over the rotated weights, bracketed by device
-    synchronisations. mode 1: the library's events bracket each call's main kernel; mode 2:
-    also the outlier-mask and row-quantization kernels. Returns (wall ms, {phase: (ms,
-    launches)})."""
+    synchronisations. mode 1: the library's events bracket each call's main kernels; mode
+    2: also the two activation quantization phases. Returns (wall ms, {phase: (ms,
+    bracketed calls)})."""
     binding.timing_read_phases()
     binding.timing_enable(mode)
     torch.cuda.synchronize()
@@ -209,14 +209,15 @@ def time_calls(binding, torch, Xd, weights, wl, n_calls: int, ws, Y, mode: int =
 
 
 def phase_breakdown(phases: dict, n_calls: int, wall_ms: float) -> dict:
-    """Per-kernel time per call (us) and its share of the call, from a mode-2 timing pass
-    (every kernel bracketed by events) whose own wall time is wall_ms."""
+    """Per-phase time per call (us) and its share of the call, from a mode-2 timing pass
+    (every phase bracketed by events) whose own wall time is wall_ms. Phases: the pass
+    over X (one kernel), the fix-up (two kernels), the main kernels (the GEMM, two
+    launches when a partial last wave of tiles is split off)."""
     out = {"pass_ms_per_call": wall_ms / n_calls}
     for name, (ms, n) in phases.items():
         if n:
             us = ms / n_calls * 1e3
-            out[name] = {"us_per_call": us, "launches_per_call": n / n_calls,
-                         "share_of_call": ms / wall_ms}
+            out[name] = {"us_per_call": us, "share_of_call": ms / wall_ms}
     return out
 
 

@@ -371,13 +371,13 @@ def read_status(workspace: torch.Tensor) -> tuple[int, int]:
 
 
 def timing_enable(on: bool | int = True) -> None:
-    """Event timing of each call's kernels: False/0 off, True/1 the main kernel, 2 also the
-    outlier-mask and row-quantization kernels (see int8mm_timing_enable)."""
+    """Event timing of each call's kernels: False/0 off, True/1 the main kernels, 2 also the
+    two activation quantization phases (see int8mm_timing_enable)."""
     _check(lib().int8mm_timing_enable(int(on)), "int8mm_timing_enable")
 
 
 def timing_read() -> tuple[float, int]:
-    """(summed main-kernel milliseconds, launches) since the last read."""
+    """(summed main-kernel milliseconds, bracketed calls) since the last read."""
     ms = ctypes.c_double(0.0)
     n = _i64(0)
     _check(lib().int8mm_timing_read(ctypes.byref(ms), ctypes.byref(n)), "int8mm_timing_read")
@@ -388,8 +388,8 @@ PHASES = ("quant_pass", "quant_fixup", "main")
 
 
 def timing_read_phases() -> dict:
-    """{phase: (summed milliseconds, launches)} since the last read, for the pass over X,
-    the quantization fix-up and the main kernel (see int8mm_timing_read_phases)."""
+    """{phase: (summed milliseconds, bracketed calls)} since the last read, for the pass
+    over X, the quantization fix-up and the main kernels (see int8mm_timing_read_phases)."""
     ms = (ctypes.c_double * 3)()
     n = (_i64 * 3)()
     _check(lib().int8mm_timing_read_phases(ms, n), "int8mm_timing_read_phases")
