@@ -385,17 +385,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     // unconditional (steps past K re-read the last unit and are not multiplied). The
     // first kEarly units go out at once, the rest when the pair's X has arrived: sent
     // together, the whole stream queues ahead of the activations in the memory system.
+    // Non-temporal loads: each weight byte is read once per call (8x4096x4096 8.20 ->
+    // 7.86 us per call).
     const int8_t* wrow =
         a.Wq + static_cast<size_t>(n0 >> 4) * ks * kUnitBytes + (lane & 15) * kUnitK + 16 * (lane >> 4);
     constexpr int E = kEarly < SPW ? kEarly : SPW;
     v4i wf[SPW];
 #pragma unroll
     for (int i = 0; i < E; ++i)
-      wf[i] = *reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes);
+      wf[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes));
     if (!lds_wait_geq(&sync_s[2 + kDecPairs + p], 1)) sync_s[kDecPairs + 1] = 1;
 #pragma unroll
     for (int i = E; i < SPW; ++i)
-      wf[i] = *reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes);
+      wf[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes));
     if (!lds_wait_geq(&sync_s[1 + p], 1)) sync_s[kDecPairs + 1] = 1;
 
     // 9. int8 MFMA: D[feature][token] += Wq[n0 + feature, k] * Xq[token, k] over the

@@ -82,6 +82,8 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < G; ++q) acc[r][q] = v4i{};
   v4i wa[kSkBatch][RG], xa[kSkBatch][G], wb[kSkBatch][RG], xb[kSkBatch][G];
+  // the weight units non-temporally (each is read once per call), the activation units
+  // cached (every block reads them)
   auto load = [&](v4i (&w)[kSkBatch][RG], v4i (&x)[kSkBatch][G], int i0) {
 #pragma unroll
     for (int b = 0; b < kSkBatch; ++b) {
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kSkThreads) void k_gemm_skinny(GemmArgs g) {
       const size_t off = static_cast<size_t>(wave + kSkWaves * (i0 + b)) * kUnitBytes;
 #pragma unroll
       for (int r = 0; r < RG; ++r)
-        w[b][r] = *reinterpret_cast<const v4i*>(in ? wrow[r] + off : zero);
+        w[b][r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(in ? wrow[r] + off : zero));
 #pragma unroll
       for (int q = 0; q < G; ++q)
         x[b][q] = *reinterpret_cast<const v4i*>(in && tok_in[q] ? xrow[q] + off : zero);

@@ -81,13 +81,15 @@ __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a)
     return tok < M && k < K ? static_cast<unsigned>(tok * K + k) * 2u : kOOB;
   };
   v4u wf[kWoBatch][RG], x0[kWoBatch], x1[kWoBatch];
+  // non-temporal weight loads: each byte is read once per call (8x4096x4096 6.12 -> 5.9 us)
   auto load_batch = [&](int base) {
 #pragma unroll
     for (int j = 0; j < kWoBatch; ++j) {
       const int s = base + kWoWaves * j;
 #pragma unroll
       for (int r = 0; r < RG; ++r)
-        wf[j][r] = *reinterpret_cast<const v4u*>(wunit[r] + static_cast<size_t>(s < ks ? s : 0) * kUnitBytes);
+        wf[j][r] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(wunit[r] + static_cast<size_t>(s < ks ? s : 0) * kUnitBytes));
       if constexpr (!XL) {
         const unsigned o = s < ks ? x_off(s) : kOOB;
         x0[j] = buf_load16(xr, o);
