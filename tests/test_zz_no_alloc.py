@@ -36,6 +36,7 @@ def _both(X, W, t=6.0, mo=256):
     ((300, 1040, 528), (40, 1040, 272)),        # prefill, then a smaller prefill
     ((2048, 4096, 16384), (8, 4096, 4096)),     # the largest workload it admits, then decode
     ((16, 4096, 1024), (3, 2048, 512)),         # decode, then a smaller decode
+    ((4000, 1040, 4400), (300, 1040, 528)),     # the GEMM in two launches, then one
 ])
 def test_noalloc_two_calls_match_workspace_call_and_oracle(first, second):
     for i, (M, K, N) in enumerate((first, second)):
