@@ -139,11 +139,15 @@ size_t int8_mixed_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_
  * (X values and Wq*w_absmax/127 rounded to fp16) with fp32 accumulation; the
  * epilogue combines both in fp32 and rounds once to fp16.
  * M <= 16 with K <= 4096, and M <= 8 with K <= 8192, run as one bandwidth-bound kernel
- * (int8_mixed_matmul_is_decode); otherwise three kernels (outlier mask, row
- * quantization + outlier gathers, MFMA GEMM). The GEMM is tiled (256 x 256, 128 x 256 or
- * 128 x 128 outputs per block, whichever is estimated fastest) or, for a few tokens (M <= 32, or M <= 64 with N K <= 2^26; K >=
- * 1024), a weight stream with one block per 16-64 output features; both compute every
- * output with the same arithmetic, so Y does not depend on which one runs.
+ * (int8_mixed_matmul_is_decode); otherwise the activation quantization (K <= 32768: one
+ * pass over X, then a two-launch fix-up for the outlier column set, the rows it changes
+ * and the outlier gathers; larger K: an outlier-mask launch, then row quantization with
+ * the gathers) and the MFMA GEMM. The GEMM is tiled (256 x 256, 128 x 256 or 128 x 128
+ * outputs per block, whichever is estimated fastest; when 256 x 256 tiles leave a partial
+ * last wave, the features that fill whole waves and the rest run as two launches) or, for
+ * a few tokens (M <= 32, or M <= 64 with N K <= 2^26; K >= 1024), a weight stream with
+ * one block per 16-64 output features; both compute every output with the same
+ * arithmetic, so Y does not depend on which one runs.
  */
 int int8_mixed_matmul(const void* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* w_absmax, int64_t N, float threshold, int64_t max_outliers,

@@ -261,7 +261,9 @@ int int8_quant_rows(const void* X, int64_t M, int64_t K, float threshold, int8_t
       !aligned16(n_outliers) || (outlier_idx && !aligned16(outlier_idx)))
     return INT8MM_E_ALIGN;
   const _Float16* x = static_cast<const _Float16*>(X);
-  hipError_t e = i8mm::launch_outlier_mask(x, int(M), int(K), threshold, 1, outlier_mask, stream);
+  // the column flags of mask_row_chunks(M, K) row chunks, merged into the caller's mask
+  hipError_t e = i8mm::launch_outlier_mask_merged(x, int(M), int(K), threshold,
+                                                  mask_row_chunks(M, K), outlier_mask, stream);
   if (e != hipSuccess) return INT8MM_E_HIP;
   i8mm::QuantRowsArgs q{};
   q.X = x; q.M = int(M); q.K = int(K);

@@ -17,6 +17,10 @@ hipError_t launch_tile_weight(const int8_t* Wnk, int K, int N, int8_t* Wq, hipSt
 // Column outlier flags: partial[rc * W + w] for row chunk rc < R, word w < W = ceil(K/32).
 hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
                                uint32_t* partial, hipStream_t s);
+// The same over R row chunks, merged into one mask [W] (cleared first, then each chunk's
+// nonzero words ORed in atomically).
+hipError_t launch_outlier_mask_merged(const _Float16* X, int M, int K, float t, int R,
+                                      uint32_t* mask, hipStream_t s);
 
 struct QuantRowsArgs {
   const _Float16* X;

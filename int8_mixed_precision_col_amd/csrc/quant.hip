@@ -30,7 +30,8 @@ namespace i8mm {
 // threshold once at the end.
 __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict__ X, int M, int K,
                                                       float t, int rpc,
-                                                      uint32_t* __restrict__ partial, int W) {
+                                                      uint32_t* __restrict__ partial, int W,
+                                                      int merge) {
   const int tid = threadIdx.x;
   const int cg = tid & 7;
   const int col0 = blockIdx.x * 64 + cg * 8;
@@ -67,8 +68,17 @@ __global__ __launch_bounds__(256) void k_outlier_mask(const _Float16* __restrict
       word |= (s[0][c] | s[1][c] | s[2][c] | s[3][c]) << (8 * g);
     }
     const int w = blockIdx.x * 2 + tid;
-    if (w < W) partial[static_cast<size_t>(blockIdx.y) * W + w] = word;
+    if (merge) {
+      if (w < W && word) atomicOr(partial + w, word);
+    } else if (w < W) {
+      partial[static_cast<size_t>(blockIdx.y) * W + w] = word;
+    }
   }
+}
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // One wave quantizes one row. CH > 0: the row is held in registers (CH chunks of 8
@@ -313,7 +323,19 @@ hipError_t launch_outlier_mask(const _Float16* X, int M, int K, float t, int R,
   const int W = (K + 31) / 32;
   const int rpc = (M + R - 1) / R;
   hipLaunchKernelGGL(k_outlier_mask, dim3((K + 63) / 64, R), dim3(256), 0, s, X, M, K, t, rpc,
-                     partial, W);
+                     partial, W, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_outlier_mask_merged(const _Float16* X, int M, int K, float t, int R,
+                                      uint32_t* mask, hipStream_t s) {
+  const int W = (K + 31) / 32;
+  const int rpc = (M + R - 1) / R;
+  hipLaunchKernelGGL(k_zero_words, dim3((W + 255) / 256), dim3(256), 0, s, mask, W);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_outlier_mask, dim3((K + 63) / 64, R), dim3(256), 0, s, X, M, K, t, rpc, mask,
+                     W, 1);
   return hipGetLastError();
 }
 
