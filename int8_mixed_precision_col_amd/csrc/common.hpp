@@ -77,29 +77,41 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned b0, unsigned b1, uns
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Exact codes of 8 halves under absmax a, for groups where the quant8_fast pair
+// Exact code of one half under absmax a (quant8_exact: 8 halves), for elements where the quant8_fast pair
 // disagreed. With w = |x| and q1 = RNE(w * lo) (lo = quant_bracket(a).lo <= 127 / a),
 // the code of w is q1 or q1 + 1; it is q1 + 1 exactly when 127 w / a > q1 + 1/2, or
 // equals it with q1 odd (half-even). That comparison, 254 w against (2 q1 + 1) a, is
 // made exactly: 254 w and (2 q1 + 1) a are exact in fp32 (18- and 19-bit products of
 // fp16 values and small integers), and one fused multiply-add gives the sign of their
 // difference. No divide; the sign of x is applied at the end.
+__device__ __forceinline__ int quant_exact1(float xf, float a, float lo) {
+  const float w = fabsf(xf);
+  const float q1 = __builtin_fmaf(w, lo, kRoundMagic) - kRoundMagic;
+  const float d = __builtin_fmaf(2.0f * q1 + 1.0f, a, -254.0f * w);
+  const int qi = static_cast<int>(q1);
+  const int q = qi + ((d < 0.0f || (d == 0.0f && (qi & 1))) ? 1 : 0);
+  return xf < 0.0f ? -q : q;
+}
 __device__ __forceinline__ v2u quant8_exact(const v8h& x, float a, float lo) {
   int c[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float xf = static_cast<float>(x[e]);
-    const float w = fabsf(xf);
-    const float q1 = __builtin_fmaf(w, lo, kRoundMagic) - kRoundMagic;
-    const float d = __builtin_fmaf(2.0f * q1 + 1.0f, a, -254.0f * w);
-    const int qi = static_cast<int>(q1);
-    const int q = qi + ((d < 0.0f || (d == 0.0f && (qi & 1))) ? 1 : 0);
-    c[e] = xf < 0.0f ? -q : q;
-  }
+  for (int e = 0; e < 8; ++e) c[e] = quant_exact1(static_cast<float>(x[e]), a, lo);
   v2u o;
   o[0] = pack4(c[0], c[1], c[2], c[3]);
   o[1] = pack4(c[4], c[5], c[6], c[7]);
   return o;
+}
+
+// Bit e set where the bracketing pair lo < 127 / a < hi rounds element e of x to two
+// different integers: the elements quant_exact1 has to settle.
+__device__ __forceinline__ unsigned quant8_disagreement(const v8h& x, float lo, float hi) {
+  unsigned em = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = static_cast<float>(x[e]);
+    em |= (__builtin_fmaf(xf, lo, kRoundMagic) != __builtin_fmaf(xf, hi, kRoundMagic) ? 1u : 0u) << e;
+  }
+  return em;
 }
 
 // Clears the halves of v whose bit is set in drop (outlier columns: their codes are 0

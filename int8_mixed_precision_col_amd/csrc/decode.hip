@@ -273,13 +273,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     // into its list segment; the count to LDS
     short* list_p = list_s + p * WCOLS;
     int wcount = 0;
-    int rfirst[CC];  // local rank of this lane's first outlier column of group j
 #pragma unroll
     for (int j = 0; j < CC; ++j) {
       const int cj = __popc(ob[j]);
       const int incl = wave_prefix_sum(cj);
-      rfirst[j] = wcount + incl - cj;
-      int r = rfirst[j];
+      int r = wcount + incl - cj;  // local rank of this lane's first outlier column
       for (unsigned bits = ob[j]; bits; bits &= bits - 1u)
         list_p[r++] = static_cast<short>((cw + lane + 64 * j) * 8 + __builtin_ctz(bits));
       wcount += __builtin_amdgcn_readlane(incl, 63);
@@ -288,9 +286,41 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       cnt_s[p] = wcount;
       __hip_atomic_fetch_add(&sync_s[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+
+    // 5. gathers for the pair's first kPre outlier columns, the epilogue's operands, sent
+    // before the meeting below so that their latency hides under the codes: the weight
+    // bytes (lane: column 4 i + l / 16 of the list, feature l % 16) and the fp16 X values
+    // (lane: column l % 16, token row l / 16 + 4 i). Which of them the epilogue takes
+    // depends on the global ranks, known after the meeting; the extra ones are unused.
+    // The list was written to LDS by this wave above, and a wave's LDS accesses complete
+    // in order.
+    constexpr int kStageLoads = kPre / 4;        // 4 columns per load (16 lanes each)
+    constexpr int kXoLoads = (MR + 3) / 4;       // 4 token rows per load
+    const int ngather = min(wcount, kPre);       // wave-uniform
+    int qv[kStageLoads];
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i) {
+      const int k = 4 * i + (lane >> 4);
+      const int col = k < ngather ? list_p[k] : 0;
+      qv[i] = a.Wq[unit_offset(n0 + (lane & 15), col, ks)];
+    }
+    // (MR <= 2: the X values are copied from the registers below instead, a divergent
+    // loop over the few lanes holding an outlier column; measured faster at one token,
+    // slower from four on)
+    constexpr bool kXoGather = MR > 2;
+    unsigned short xg[kXoLoads];
+    if constexpr (kXoGather) {
+      const int k = lane & 15;
+      const int col = k < ngather ? list_p[k] : 0;
+#pragma unroll
+      for (int i = 0; i < kXoLoads; ++i) {
+        const int m = min((lane >> 4) + 4 * i, M - 1);
+        xg[i] = reinterpret_cast<const unsigned short*>(a.X)[static_cast<size_t>(m) * K + col];
+      }
+    }
     if (!lds_wait_geq(&sync_s[0], kDecPairs)) sync_s[kDecPairs + 1] = 1;
 
-    // 5. row constants: lane r combines row r's maxima over the pairs and takes its
+    // 6. row constants: lane r combines row r's maxima over the pairs and takes its
     // quantization bracket; the rows' values are read from those lanes below
     float am_l;
     QuantBracket br_l;
@@ -306,29 +336,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     int first = 0;  // first global rank of this pair
 #pragma unroll
     for (int w = 0; w < kDecPairs; ++w) first += w < p ? cnt_s[w] : 0;
-
-    // 6. the pair's outlier columns of global rank < kPre, for the epilogue: their fp16 X
-    // values from the registers (a divergent loop over the lanes holding one), and their
-    // weight bytes, loaded now (lane: rank first + 4 i + l / 16, feature l % 16) so that
-    // the latency hides under the codes
+    if constexpr (!kXoGather) {
 #pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      int r = first + rfirst[j];
-      for (unsigned bits = ob[j]; bits && r < kPre; bits &= bits - 1u, ++r) {
-        const int e = __builtin_ctz(bits);
+      for (int j = 0; j < CC; ++j) {
+        const int cj = __popc(ob[j]);
+        const int incl = wave_prefix_sum(cj);
+        int r = first + incl - cj;  // global rank of this lane's first outlier column
+        for (unsigned bits = ob[j]; bits && r < kPre; bits &= bits - 1u, ++r) {
+          const int e = __builtin_ctz(bits);
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
-          if (m < M) xo_s[r * 16 + m] = half_bits_to_float(half_at(xv[m][j], e));
+          for (int m = 0; m < MR; ++m)
+            if (m < M) xo_s[r * 16 + m] = half_bits_to_float(half_at(xv[m][j], e));
+        }
       }
-    }
-    const int nstage = max(0, min(wcount, kPre - first));  // wave-uniform
-    constexpr int kStageLoads = kPre / 4;  // 4 columns per load (16 lanes each)
-    int qv[kStageLoads];
-#pragma unroll
-    for (int i = 0; i < kStageLoads; ++i) {
-      const int k = 4 * i + (lane >> 4);
-      const int col = k < nstage ? list_p[k] : 0;
-      qv[i] = a.Wq[unit_offset(n0 + (lane & 15), col, ks)];
     }
 
     // 7. codes of this pair's columns into its LDS rows, outlier columns cleared (their
@@ -353,8 +373,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
         *reinterpret_cast<v2u*>(lc < WCH ? xq_p + m * XS + lc * 8 : sink) = o;
       }
     }
-    // 8. exact codes (values at or within about 2^-15 of a half-integer, exact ties
-    // included, make the pair disagree): wave-uniform branches, rarely taken
+    // 8. exact codes where the pair disagreed (values at or within about 2^-15 of a
+    // half-integer, exact ties included: in fp16 data every element equal to half its
+    // row's absmax is one): per (row, chunk) slot with a disagreement, a wave-uniform
+    // branch; in it each lane finds which of its 8 elements disagree and settles them one
+    // at a time, each with an exact comparison, its code stored as one byte
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
@@ -362,18 +385,35 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
         if (dm[m][j] != 0) {
           const float am = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, am_l), m));
           const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.lo), m));
+          const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, br_l.hi), m));
           const int lc = lane + 64 * j;
-          if ((dm[m][j] >> lane) & 1u)
-            *reinterpret_cast<v2u*>(lc < WCH ? xq_p + m * XS + lc * 8 : sink) = quant8_exact(xv[m][j], am, lo);
+          unsigned em = (dm[m][j] >> lane) & 1u ? quant8_disagreement(xv[m][j], lo, hi) : 0u;
+          int8_t* row = lc < WCH ? xq_p + m * XS + lc * 8 : sink;
+          while (__ballot(em != 0u) != 0) {  // wave-uniform
+            if (em != 0u) {
+              const int e = __builtin_ctz(em);
+              em &= em - 1u;
+              row[e] = static_cast<int8_t>(quant_exact1(half_bits_to_float(half_at(xv[m][j], e)), am, lo));
+            }
+          }
         }
-    // the staged weights: W^ = fp16(q a_w / 127), the int8 weight dequantized as the GEMM
-    // epilogue forms it
+    // the gathered operands of the pair's outlier columns of global rank < kPre: X as
+    // fp32, and W^ = fp16(q a_w / 127), the int8 weight dequantized as the GEMM epilogue
+    // forms it
+    const int nstage = max(0, min(wcount, kPre - first));  // wave-uniform
 #pragma unroll
     for (int i = 0; i < kStageLoads; ++i) {
       const int k = 4 * i + (lane >> 4);
       if (k < nstage)
         wo_s[(first + k) * 16 + (lane & 15)] =
             static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv[i]) * aw_c, 127.0f)));
+    }
+    if constexpr (kXoGather) {
+#pragma unroll
+      for (int i = 0; i < kXoLoads; ++i) {
+        const int k = lane & 15, m = (lane >> 4) + 4 * i;
+        if (k < nstage && m < M) xo_s[(first + k) * 16 + m] = half_bits_to_float(xg[i]);
+      }
     }
     if (lane == 0)
       __hip_atomic_fetch_add(&sync_s[1 + p], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
