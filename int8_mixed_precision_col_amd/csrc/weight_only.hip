@@ -10,8 +10,9 @@
 // output.
 //
 // One block per 16 RG output features (RG 16-row groups of the unit-tiled Wq; RG = 2
-// where N leaves more than 256 blocks of 16, so that fewer blocks re-read X), 16 waves.
-// Wave w takes k-steps w, w + 16, ... (64 columns each) in batches of kWoBatch; per
+// where N leaves more than 256 blocks of 16, so that fewer blocks re-read X), W waves:
+// 8 (16 where RG = 2). Wave w takes k-steps w, w + W, ... (64 columns each) in batches of
+// kWoBatch (8; 2 where RG = 2), the batch's loads in flight together; per
 // step every lane loads one 16-byte slice of the step's 1 KB weight unit and the two
 // 8-column pieces of X (its token, the same columns) that the MFMAs pair with it,
 // straight into registers: no staging, no barrier before the products. X loads go
@@ -24,8 +25,6 @@
 #include "launch.hpp"
 
 namespace i8mm {
-
-constexpr int kWoWaves = 16, kWoBatch = 4;
 
 // 4 int8 codes (one dword) -> 4 fp16 of the same values, as 2 dwords.
 __device__ __forceinline__ v2u int8x4_to_half(unsigned d) {
@@ -48,8 +47,9 @@ __device__ __forceinline__ v2u int8x4_to_half(unsigned d) {
 // row segments) and M x K x 2 <= kWoXLdsMax bytes.
 constexpr int kWoXLdsMax = 64 << 10;
 
-template <int RG, bool XL>
+template <int RG, bool XL, int kWoWaves, int kWoBatch>
 __global__ __launch_bounds__(64 * kWoWaves) void k_weight_only(WeightOnlyArgs a) {
+  static_assert(kWoBatch * RG + 1 <= 15, "the X-staging wait counts loads in 4 bits");
   __shared__ float red[kWoWaves][16 * RG][17];
   extern __shared__ __attribute__((aligned(16))) char xs[];  // XL: [M][2 K + 16]
   const int K = a.K, M = a.M, N = a.N;
@@ -161,16 +161,18 @@ bool weight_only_supported(int64_t M, int64_t K) {
 // 512 groups of 16 on (4 x 8192 x 8192: 14.8-15.0 against 16.2 us with 16 per block;
 // 8 x 4096 x 4096: 7.0 against 6.2 us); X staged in LDS pays with many tokens (16 x 2048
 // x 4096: 4.8 against 5.7 us) and costs its barrier with few (8 x 4096 x 4096: 6.45
-// against 6.2 us).
+// against 6.2 us). Waves x batch: 8 x 8 against 16 x 4 at one row group per block
+// (8 x 4096 x 4096 5.62 against 5.83 us, 1 x 4096^2 4.88 against 5.02, 16 x 4096^2 6.95
+// against 7.13), 16 x 2 at two (4 x 8192 x 8192 13.9 against 15.5 us; 8 x 8 17.6).
 hipError_t launch_weight_only(const WeightOnlyArgs& a, hipStream_t s) {
   const int nrg = a.N / 16;
   if (nrg > 256) {
-    hipLaunchKernelGGL((k_weight_only<2, false>), dim3((nrg + 1) / 2), dim3(64 * kWoWaves), 0, s, a);
+    hipLaunchKernelGGL((k_weight_only<2, false, 16, 2>), dim3((nrg + 1) / 2), dim3(64 * 16), 0, s, a);
   } else if (a.M >= 12 && a.K % 512 == 0 && static_cast<int64_t>(a.M) * a.K * 2 <= kWoXLdsMax) {
     const size_t lds = static_cast<size_t>(a.M) * (2 * a.K + 16);
-    hipLaunchKernelGGL((k_weight_only<1, true>), dim3(nrg), dim3(64 * kWoWaves), lds, s, a);
+    hipLaunchKernelGGL((k_weight_only<1, true, 8, 8>), dim3(nrg), dim3(64 * 8), lds, s, a);
   } else {
-    hipLaunchKernelGGL((k_weight_only<1, false>), dim3(nrg), dim3(64 * kWoWaves), 0, s, a);
+    hipLaunchKernelGGL((k_weight_only<1, false, 8, 8>), dim3(nrg), dim3(64 * 8), 0, s, a);
   }
   return hipGetLastError();
 }
