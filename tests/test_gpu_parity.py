@@ -241,6 +241,22 @@ def test_decode_every_instantiation(M, K):
     check_y(Y, ref["Y"])
 
 
+@pytest.mark.parametrize("M,K", [(1, 1024), (2, 4000), (3, 2048), (8, 4096), (16, 1040)])
+def test_decode_many_outlier_columns(M, K):
+    """More outlier columns than the decode kernel stages while it makes the codes (16),
+    spread over every pair of waves: the first 16 come from the staged values (copied
+    from registers at one or two tokens, gathered from X and Wq from three on), the rest
+    from the epilogue's later passes; the ascending order of the outlier sum is kept."""
+    assert binding.is_decode(M, K)
+    announce(f"decode many outliers M={M} K={K}")
+    X = planted(11 * M + K, M, K, n_dims=40, frac=1.0)
+    W = weight(K + 3, K, 48)
+    ref, Y, acc = _mixed(X, W, 6.0, mo=256)
+    assert ref["count"] == 40
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
 @pytest.mark.parametrize("M,K,N", [(2048, 1024, 64), (600, 2000, 48)])
 def test_lone_outlier_rows_in_every_row_chunk(M, K, N):
     """Each outlier column holds one large value in a single row (first, middle and last
