@@ -202,8 +202,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   if (wave < kDecPairs) {
     // ---------------------------------------------------------------- compute wave p
     const int cw = WCH * p;  // first chunk of this pair
-    // 1. X. Rows past M read the last row and chunks outside the pair's range or past K
-    // the last chunk: repeats change no maximum; such chunks are masked out below.
+    // 1. X. Chunks outside the pair's range or past K read the last chunk (repeats change
+    // no maximum; such chunks are masked out below); rows past M read zeros through the
+    // buffer resource's range check, without a memory access, so that they add nothing
+    // to the maxima and quantize to 0 with no exact work.
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, static_cast<unsigned>(M) * K * 2u);
     v8h xv[MR][CC];
     bool cval[CC];
 #pragma unroll
@@ -213,7 +216,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       const int cc = min(c, nchunk - 1);
 #pragma unroll
       for (int m = 0; m < MR; ++m)
-        xv[m][j] = *reinterpret_cast<const v8h*>(a.X + static_cast<size_t>(min(m, M - 1)) * K + cc * 8);
+        xv[m][j] = __builtin_bit_cast(
+            v8h, buf_load16(xr, m < M ? static_cast<unsigned>(m * K + cc * 8) * 2u : kOOB));
     }
     aw_c = a.a_w[n0 + (tid & 15)];
     if (tid == 0)
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     }
 
     // 7. codes of this pair's columns into its LDS rows, outlier columns cleared (their
-    // codes are 0). Rows past M hold copies of row M - 1 and fill the scratch rows. The
+    // codes are 0). Rows past M (zeros) fill the scratch rows. The
     // bracketing pair decides; (row, chunk) slots where it disagrees in some lane are
     // redone with quant8_exact below.
     unsigned long long dm[MR][CC];  // lanes where the pair disagreed
