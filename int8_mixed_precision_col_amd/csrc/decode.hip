@@ -3,8 +3,9 @@
 // "What is 8-bit LLM quantization?", Does INT8 always improve speed?: at decode time the
 // gain of int8 weights is the smaller weight stream. With M <= 16 tokens the N x K
 // bytes of Wq are the whole cost, so one launch does every step and reads each Wq byte
-// from HBM exactly once. One block per 16 output features, all of K, 16 waves in 8
-// pairs; pair p owns the K-steps (64 columns each) SPW p .. SPW p + SPW - 1:
+// from HBM exactly once. One block per 16 output features, all of K, P pairs of waves (8;
+// 2 for 513-1024 columns of K, 4 for 1025-2048); pair p owns the K-steps (64 columns
+// each) SPW p .. SPW p + SPW - 1:
 //   * compute wave p loads the 8-column chunks of X of exactly those columns for every
 //     token row (these requests go out first: the stream wave of the pair sends only a
 //     few weight requests until this X has arrived), finds the outlier columns among
@@ -38,10 +39,8 @@
 namespace i8mm {
 
 constexpr int kDecMaxM = 16, kDecMaxK = 8192;
-constexpr int kDecPairs = 8;                      // compute waves = stream waves
-constexpr int kDecThreads = 2 * 64 * kDecPairs;   // 1024
 constexpr int kPre = 16;    // outlier columns staged while the codes are made
-constexpr int kChunkO = 32; // outlier columns per later epilogue pass
+constexpr int kChunkO = 32; // outlier columns per later epilogue pass (at most)
 #ifndef I8MM_DEC_EARLY
 #define I8MM_DEC_EARLY 2
 #endif
@@ -58,9 +57,21 @@ static int pow2_at_least(int v) {
 }
 // token rows held per thread: M rounded up to a power of two
 static int rows_held(int64_t M) { return pow2_at_least(static_cast<int>(M)); }
-// K-steps (64 columns) per pair: ceil(ceil(K / 64) / 8) rounded up to a power of two
-static int steps_per_wave(int64_t K) {
-  return pow2_at_least(static_cast<int>((unit_ks(static_cast<int>(K)) + kDecPairs - 1) / kDecPairs));
+// Pairs of waves per block (compute waves = stream waves): 8, or fewer where K leaves a
+// pair fewer than 8 K-steps and at least 4 token rows are held, so that every lane of a
+// compute wave owns a chunk: a wave issues the same instructions however many of its
+// lanes hold data, and with 4-16 rows the activation phase is bound by the instructions
+// each SIMD issues (9-16 K-steps: 2 pairs, 17-32: 4). With 1-2 rows the work is small and
+// 8 pairs, more loads in flight, measured faster.
+static int decode_pairs(int64_t M, int64_t K) {
+  const int ks = unit_ks(static_cast<int>(K));
+  if (rows_held(M) < 4) return 8;
+  return ks > 8 && ks <= 16 ? 2 : ks > 16 && ks <= 32 ? 4 : 8;
+}
+// K-steps (64 columns) per pair: ceil(ceil(K / 64) / pairs) rounded up to a power of two
+static int steps_per_wave(int64_t M, int64_t K) {
+  const int P = decode_pairs(M, K);
+  return pow2_at_least(static_cast<int>((unit_ks(static_cast<int>(K)) + P - 1) / P));
 }
 
 // X chunks a thread holds in registers: rows_held(M) x (1, or 2 past 4096 columns), at
@@ -74,8 +85,8 @@ bool decode_supported(int64_t M, int64_t K) {
 // scratch), the outlier column lists (one segment of 64 SPW shorts per pair), and a sink of
 // 8 bytes per lane for the code stores of lanes that own no chunk.
 static size_t decode_lds_bytes(int64_t M, int64_t K) {
-  const size_t spw = static_cast<size_t>(steps_per_wave(K));
-  return kDecPairs * static_cast<size_t>(rows_held(M)) * (64 * spw + 16) + kDecPairs * 64 * spw * 2 + 64 * 8;
+  const size_t spw = static_cast<size_t>(steps_per_wave(M, K)), P = static_cast<size_t>(decode_pairs(M, K));
+  return P * static_cast<size_t>(rows_held(M)) * (64 * spw + 16) + P * 64 * spw * 2 + 64 * 8;
 }
 
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
@@ -121,10 +132,11 @@ __device__ __forceinline__ void wave_max_u32_n(unsigned (&v)[N]) {
 
 // The pair holding outlier rank r (0 <= r < count): the last pair whose first rank is at
 // most r (wb: first rank of each pair, nondecreasing).
-__device__ __forceinline__ int pair_of_rank(const int (&wb)[kDecPairs + 1], int r) {
+template <int P>
+__device__ __forceinline__ int pair_of_rank(const int (&wb)[P + 1], int r) {
   int w = 0;
 #pragma unroll
-  for (int i = 1; i < kDecPairs; ++i) w += r >= wb[i] ? 1 : 0;
+  for (int i = 1; i < P; ++i) w += r >= wb[i] ? 1 : 0;
   return w;
 }
 
@@ -172,8 +184,10 @@ __device__ __forceinline__ bool lds_wait_geq(int* counter, int target) {
 
 // MR: token rows held per compute thread (M <= MR). SPW: K-steps per pair; a compute
 // lane owns the chunks c = 8 SPW p + l + 64 j (j < CC) of every row.
-template <int MR, int SPW>
-__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
+template <int MR, int SPW, int P>
+__global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
+  constexpr int kDecPairs = P;
+  constexpr int CO = kChunkO < 8 * P ? kChunkO : 8 * P;  // later epilogue pass: 16 CO threads
   constexpr int CC = SPW > 8 ? SPW / 8 : 1;  // chunks per lane
   constexpr int WCH = 8 * SPW;               // chunks per pair
   constexpr int WCOLS = 64 * SPW;            // columns per pair
@@ -197,7 +211,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   int8_t* xq_p = reinterpret_cast<int8_t*>(lds) + p * MR * XS;  // pair p's codes [MR][XS]
   short* list_s = reinterpret_cast<short*>(lds + kDecPairs * MR * XS);
   int8_t* sink = reinterpret_cast<int8_t*>(list_s + kDecPairs * WCOLS) + lane * 8;
-  float aw_c = 0.0f;  // the epilogue's column constant (compute waves)
+  // the epilogue's column constant of feature n0 + t % 16: loaded by the compute waves,
+  // and with fewer than 8 pairs by the stream waves too (the epilogue's threads, and its
+  // later outlier passes, then span both)
+  float aw_c = 0.0f;
 
   if (wave < kDecPairs) {
     // ---------------------------------------------------------------- compute wave p
@@ -444,6 +461,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     for (int i = E; i < SPW; ++i)
       wf[i] = __builtin_nontemporal_load(
           reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes));
+    if constexpr (kDecPairs < 8) aw_c = a.a_w[n0 + (tid & 15)];
     if (!lds_wait_geq(&sync_s[1 + p], 1)) sync_s[kDecPairs + 1] = 1;
 
     // 9. int8 MFMA: D[feature][token] += Wq[n0 + feature, k] * Xq[token, k] over the
@@ -465,7 +483,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 
   // 11. epilogue: thread t < 256 -> (token m, output feature n0 + nl). The int32 partials
   // of the pairs are summed exactly; the outlier product in fp32, ascending columns, the
-  // first kPre from the staged values, the rest kChunkO at a time from global memory.
+  // first kPre from the staged values, the rest CO at a time from global memory.
   int wb[kDecPairs + 1];
   wb[0] = 0;
 #pragma unroll
@@ -476,14 +494,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   float yo = 0.0f;
   if (tid < 256)
     for (int r = 0; r < npre; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
-  for (int r0 = kPre; r0 < count; r0 += kChunkO) {  // block-uniform trip count
+  for (int r0 = kPre; r0 < count; r0 += CO) {  // block-uniform trip count
     lds_barrier();  // the staged values above are read
-    const int rn = min(kChunkO, count - r0);
-    if (tid < kChunkO * 16) {
+    const int rn = min(CO, count - r0);
+    if (tid < CO * 16) {
       const int pr = tid >> 4, pq = tid & 15;
       int col = 0;
       if (pr < rn) {
-        const int w = pair_of_rank(wb, r0 + pr);
+        const int w = pair_of_rank<kDecPairs>(wb, r0 + pr);
         col = list_s[w * WCOLS + r0 + pr - wb[w]];
       }
       const int q = a.Wq[unit_offset(n0 + pq, col, ks)];
@@ -516,18 +534,20 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const size_t lds = decode_lds_bytes(a.M, a.K);
-  const int mr = rows_held(a.M), spw = steps_per_wave(a.K);
-  const dim3 grid(a.N / 16), block(kDecThreads);
-#define I8MM_DEC(R, P)                                                   \
-  if (mr == R && spw == P) {                                             \
-    hipLaunchKernelGGL((k_decode<R, P>), grid, block, lds, s, a);        \
+  const int mr = rows_held(a.M), spw = steps_per_wave(a.M, a.K), pairs = decode_pairs(a.M, a.K);
+  const dim3 grid(a.N / 16), block(128 * pairs);
+#define I8MM_DEC(R, W, P)                                                \
+  if (mr == R && spw == W && pairs == P) {                               \
+    hipLaunchKernelGGL((k_decode<R, W, P>), grid, block, lds, s, a);     \
     return hipGetLastError();                                            \
   }
-  I8MM_DEC(1, 1) I8MM_DEC(1, 2) I8MM_DEC(1, 4) I8MM_DEC(1, 8) I8MM_DEC(1, 16)
-  I8MM_DEC(2, 1) I8MM_DEC(2, 2) I8MM_DEC(2, 4) I8MM_DEC(2, 8) I8MM_DEC(2, 16)
-  I8MM_DEC(4, 1) I8MM_DEC(4, 2) I8MM_DEC(4, 4) I8MM_DEC(4, 8) I8MM_DEC(4, 16)
-  I8MM_DEC(8, 1) I8MM_DEC(8, 2) I8MM_DEC(8, 4) I8MM_DEC(8, 8) I8MM_DEC(8, 16)
-  I8MM_DEC(16, 1) I8MM_DEC(16, 2) I8MM_DEC(16, 4) I8MM_DEC(16, 8)
+  I8MM_DEC(1, 1, 8) I8MM_DEC(1, 2, 8) I8MM_DEC(1, 4, 8) I8MM_DEC(1, 8, 8) I8MM_DEC(1, 16, 8)
+  I8MM_DEC(2, 1, 8) I8MM_DEC(2, 2, 8) I8MM_DEC(2, 4, 8) I8MM_DEC(2, 8, 8) I8MM_DEC(2, 16, 8)
+  I8MM_DEC(4, 1, 8) I8MM_DEC(4, 2, 8) I8MM_DEC(4, 4, 8) I8MM_DEC(4, 8, 8) I8MM_DEC(4, 16, 8)
+  I8MM_DEC(8, 1, 8) I8MM_DEC(8, 2, 8) I8MM_DEC(8, 4, 8) I8MM_DEC(8, 8, 8) I8MM_DEC(8, 16, 8)
+  I8MM_DEC(16, 1, 8) I8MM_DEC(16, 2, 8) I8MM_DEC(16, 4, 8) I8MM_DEC(16, 8, 8)
+  I8MM_DEC(4, 8, 2) I8MM_DEC(8, 8, 2) I8MM_DEC(16, 8, 2)
+  I8MM_DEC(4, 8, 4) I8MM_DEC(8, 8, 4) I8MM_DEC(16, 8, 4)
 #undef I8MM_DEC
   return hipErrorInvalidValue;
 }

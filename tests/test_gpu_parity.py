@@ -227,7 +227,11 @@ def test_largest_k_extreme_accumulators():
 DECODE_SHAPES = [(2, 528), (1, 2000), (2, 4000), (1, 8000), (3, 1008), (4, 1552), (3, 4080),
                  (4, 8192), (6, 992), (7, 2032), (5, 4096), (6, 5456), (12, 720), (11, 1792),
                  (10, 3264),
-                 (7, 7008), (8, 8192), (13, 3600), (16, 4096)]
+                 (7, 7008), (8, 8192), (13, 3600), (16, 4096),
+                 # one or two rows at 513-2048 columns (8 pairs of waves there; from 3 rows
+                 # on, 2 or 4 pairs: (3, 1008), (6, 992), (12, 720), (4, 1552), (7, 2032),
+                 # (11, 1792) above)
+                 (1, 1008), (2, 1104)]
 
 
 @pytest.mark.parametrize("M,K", DECODE_SHAPES)
