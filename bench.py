@@ -306,9 +306,42 @@ def bench_config(binding, torch, inputs, name: str, calls: int = 20, warmup: int
         alg = wl.M * wl.K * 2 + wl.N * wl.K + wl.N * 4 + wl.M * wl.N * 2
         res["main_kernel"]["GB/s"] = alg / (main_ms * 1e-3) / 1e9
         res["main_kernel"]["frac_of_hbm_peak"] = res["main_kernel"]["GB/s"] / PEAK_HBM_GBS
+        # the same calls captured in one HIP graph, as for the decode line: per call without
+        # the host's launch overhead
+        g_us = graph_per_call_us(binding, torch, Xd, weights, wl, ws, Y)
+        res["graph"] = {"us_per_call": g_us, "GB/s": alg / (g_us * 1e-6) / 1e9,
+                        "frac_of_hbm_peak": alg / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "note": f"{len(weights)} calls over the rotated weights in one graph"}
     del Xd, weights, ws, Y
     torch.cuda.empty_cache()
     return res
+
+
+def graph_per_call_us(binding, torch, Xd, weights, wl, ws, Y, reps: int = 20) -> float:
+    """int8_mixed_matmul once per prepared weight, captured in one HIP graph and replayed
+    reps times between events; per-call time = replay time / calls. The last output is
+    checked against an eager call on the same weight."""
+    Y_ref = binding.mixed_matmul(Xd, *weights[-1], wl.threshold, MAX_OUTLIERS, workspace=ws).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for Wq, aw in weights[:2]:
+            binding.mixed_matmul(Xd, Wq, aw, wl.threshold, MAX_OUTLIERS, workspace=ws, out=Y)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for Wq, aw in weights:
+            binding.mixed_matmul(Xd, Wq, aw, wl.threshold, MAX_OUTLIERS, workspace=ws, out=Y)
+    for _ in range(3):
+        graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_ref), "graph replay differs from the eager call"
+    return e0.elapsed_time(e1) / (reps * len(weights)) * 1e3
 
 
 def measured_copy_floor(torch, nbytes: int = 8 << 20, copies: int = 32, reps: int = 20) -> dict:
