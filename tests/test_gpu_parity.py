@@ -245,12 +245,15 @@ def test_decode_every_instantiation(M, K):
     check_y(Y, ref["Y"])
 
 
-@pytest.mark.parametrize("M,K", [(1, 1024), (2, 4000), (3, 2048), (8, 4096), (16, 1040)])
+@pytest.mark.parametrize("M,K", [(1, 1024), (2, 4000), (3, 2048), (8, 4096), (16, 1040),
+                                 # two pairs of waves: later outlier passes of 16 columns
+                                 (4, 1024), (16, 960)])
 def test_decode_many_outlier_columns(M, K):
     """More outlier columns than the decode kernel stages while it makes the codes (16),
     spread over every pair of waves: the first 16 come from the staged values (copied
     from registers at one or two tokens, gathered from X and Wq from three on), the rest
-    from the epilogue's later passes; the ascending order of the outlier sum is kept."""
+    from the epilogue's later passes (32 columns a pass, 16 with two pairs of waves); the
+    ascending order of the outlier sum is kept."""
     assert binding.is_decode(M, K)
     announce(f"decode many outliers M={M} K={K}")
     X = planted(11 * M + K, M, K, n_dims=40, frac=1.0)
