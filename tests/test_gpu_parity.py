@@ -299,7 +299,9 @@ def test_zero_outlier_invariant(M, K, N):
     check_y(Y, ref["y_int8"].astype(np.float16))
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 512, 128), (96, 528, 272), (40, 1024, 272)])
+@pytest.mark.parametrize("M,K,N", [(16, 512, 128), (96, 528, 272), (40, 1024, 272),
+                                   # decode kernel with two and four pairs of waves
+                                   (16, 1024, 64), (8, 2048, 64)])
 def test_all_outlier_invariant(M, K, N):
     """t = 0: every column is an outlier; with a lossless int8 weight, Y = fp16(X @ W)."""
     announce(f"all-outlier invariant M={M} K={K} N={N}")
