@@ -70,6 +70,35 @@ static hipError_t run_grouped(GroupedGemmArgs& a, hipStream_t s, int group_m) {
   return hipGetLastError();
 }
 
+static hipError_t run_grouped_tile(Tile t, GroupedGemmArgs& a, hipStream_t s) {
+  if (t == Tile::L) return run_grouped<CfgL>(a, s, 8);
+  if (t == Tile::M) return run_grouped<CfgM>(a, s, 8);
+  return run_grouped<CfgS>(a, s, 8);
+}
+
+// Groups [q0, q1) of a as a grouped product of their own.
+static GroupedGemmArgs group_range(const GroupedGemmArgs& a, int q0, int q1) {
+  GroupedGemmArgs r = a;
+  r.G = q1 - q0;
+  for (int q = 0; q < r.G; ++q) {
+    r.Wq[q] = a.Wq[q0 + q];
+    r.a_w[q] = a.a_w[q0 + q];
+    r.Y[q] = a.Y[q0 + q];
+    r.N[q] = a.N[q0 + q];
+  }
+  return r;
+}
+
+// Cost, in waves of 256 x 256 tiles, of the best single tile shape for the tile counts
+// tiles(tn, tm).
+template <class F>
+static double best_cost(F tiles, Tile* t) {
+  *t = pick_tile(tiles);
+  if (*t == Tile::L) return wave_cost(tiles(256, 256));
+  if (*t == Tile::M) return wave_cost(tiles(128, 256)) * (0.5 / 0.9);
+  return wave_cost(tiles(128, 128)) * (0.25 / 0.85);
+}
+
 // Same choice of kernel and tile shape as launch_gemm, on the combined tile count. A
 // handful of tokens takes the skinny kernel once per weight: its blocks fill the GPU
 // at any width, and each output is then computed exactly as by the one-weight call.
@@ -88,14 +117,43 @@ hipError_t launch_gemm_grouped(GroupedGemmArgs& a, hipStream_t s) {
     }
     return hipSuccess;
   }
-  const Tile t = pick_tile([&](int tn, int tm) {
-    long n = 0;
-    for (int q = 0; q < a.G; ++q) n += static_cast<long>((a.N[q] + tn - 1) / tn) * ((a.base.M + tm - 1) / tm);
-    return n;
-  });
-  if (t == Tile::L) return run_grouped<CfgL>(a, s, 8);
-  if (t == Tile::M) return run_grouped<CfgM>(a, s, 8);
-  return run_grouped<CfgS>(a, s, 8);
+  // tile count of groups [q0, q1) for tiles of tn features x tm tokens
+  auto tiles_in = [&](int q0, int q1) {
+    return [&a, q0, q1](int tn, int tm) {
+      long n = 0;
+      for (int q = q0; q < q1; ++q) n += static_cast<long>((a.N[q] + tn - 1) / tn) * ((a.base.M + tm - 1) / tm);
+      return n;
+    };
+  };
+  const Tile t = pick_tile(tiles_in(0, a.G));
+  // A split at a group boundary, as launch_gemm splits a product: when the leading groups'
+  // 256 x 256 tiles fill whole waves and the single launch would end on a partial wave,
+  // the leading groups take one launch of 256 x 256 tiles and the rest a second launch
+  // with the shape that suits them. The grouped epilogue dequantizes the outlier columns'
+  // weights in every tile, and a partial last wave measured costlier here than on the
+  // one-weight path (Q, K, V of 2048 x 4096: half a wave took 0.77 of a full one; the
+  // split took the grouped GEMM from 114.6 to 107.3 us), so the single launch's partial
+  // wave is counted as at least 0.75 of a wave.
+  if (t == Tile::L) {
+    const long cus = device_cus(), total = tiles_in(0, a.G)(256, 256);
+    const double w = static_cast<double>(total) / cus, full = static_cast<double>(total / cus);
+    const double single = full + (w > full ? (w - full > 0.75 ? w - full : 0.75) : 0.0);
+    long lead = 0;
+    for (int j = 1; j < a.G && total % cus != 0; ++j) {
+      lead += tiles_in(j - 1, j)(256, 256);
+      if (lead % cus != 0) continue;
+      Tile t2;
+      const double split = static_cast<double>(lead / cus) + best_cost(tiles_in(j, a.G), &t2) + 0.05;
+      if (split < single) {
+        GroupedGemmArgs a1 = group_range(a, 0, j), a2 = group_range(a, j, a.G);
+        const hipError_t e = run_grouped<CfgL>(a1, s, 8);
+        if (e != hipSuccess) return e;
+        return run_grouped_tile(t2, a2, s);
+      }
+      break;
+    }
+  }
+  return run_grouped_tile(t, a, s);
 }
 
 // Features [n0, n1) of the product g as a product of its own (n0 a multiple of 16: the
@@ -120,11 +178,7 @@ static hipError_t run_tile(Tile t, const GemmArgs& g, hipStream_t s) {
 
 // Cost, in waves of 256 x 256 tiles, of the best single tile shape over M x N.
 static double best_cost(long M, long N, Tile* t) {
-  auto tiles = [&](int tn, int tm) { return ((N + tn - 1) / tn) * ((M + tm - 1) / tm); };
-  *t = pick_tile(tiles);
-  if (*t == Tile::L) return wave_cost(tiles(256, 256));
-  if (*t == Tile::M) return wave_cost(tiles(128, 256)) * (0.5 / 0.9);
-  return wave_cost(tiles(128, 128)) * (0.25 / 0.85);
+  return best_cost([&](int tn, int tm) { return ((N + tn - 1) / tn) * ((M + tm - 1) / tm); }, t);
 }
 
 // A last, partial wave of 256 x 256 tiles leaves CUs idle for a whole tile's time (the
