@@ -3,8 +3,9 @@
 // "What is 8-bit LLM quantization?", Does INT8 always improve speed?: at decode time the
 // gain of int8 weights is the smaller weight stream. With M <= 16 tokens the N x K
 // bytes of Wq are the whole cost, so one launch does every step and reads each Wq byte
-// from HBM exactly once. One block per 16 output features, all of K, P pairs of waves (8;
-// 2 for 513-1024 columns of K, 4 for 1025-2048); pair p owns the K-steps (64 columns
+// from HBM exactly once. One block per 16 output features (32 where N has more 16-row
+// groups than the GPU has CUs and 5-8 token rows are held), all of K, P pairs of waves
+// (8; 2 for 513-1024 columns of K, 4 for 1025-2048); pair p owns the K-steps (64 columns
 // each) SPW p .. SPW p + SPW - 1:
 //   * compute wave p loads the 8-column chunks of X of exactly those columns for every
 //     token row (these requests go out first: the stream wave of the pair sends only a
@@ -183,21 +184,26 @@ __device__ __forceinline__ bool lds_wait_geq(int* counter, int target) {
 }
 
 // MR: token rows held per compute thread (M <= MR). SPW: K-steps per pair; a compute
-// lane owns the chunks c = 8 SPW p + l + 64 j (j < CC) of every row.
-template <int MR, int SPW, int P>
+// lane owns the chunks c = 8 SPW p + l + 64 j (j < CC) of every row. RG: 16-row groups of
+// Wq per block (2 where N leaves more row groups than the GPU has CUs, at most 8 K-steps
+// per pair and 8 rows held: one activation pass then serves 32 output features). The
+// two-group form differs in the stream waves, the staged outlier weights and the
+// epilogue; each of those has its own branch below, the one-group code unchanged.
+template <int MR, int SPW, int P, int RG>
 __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
   constexpr int kDecPairs = P;
+  constexpr int NF = 16 * RG;  // output features per block
   constexpr int CO = kChunkO < 8 * P ? kChunkO : 8 * P;  // later epilogue pass: 16 CO threads
   constexpr int CC = SPW > 8 ? SPW / 8 : 1;  // chunks per lane
   constexpr int WCH = 8 * SPW;               // chunks per pair
   constexpr int WCOLS = 64 * SPW;            // columns per pair
   constexpr int XS = WCOLS + 16;             // code row stride (padding: conflict-free reads)
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int red[kDecPairs][16][17];
+  __shared__ int red[kDecPairs][NF][17];
   __shared__ unsigned rmax_s[kDecPairs][16];
   __shared__ int cnt_s[kDecPairs];
   __shared__ float rowmax_s[16];
-  __shared__ float xo_s[kChunkO * 16], wo_s[kChunkO * 16];
+  __shared__ float xo_s[kChunkO * 16], wo_s[kChunkO * NF];
   // [0]: compute waves past their row maxima; [1 + p]: pair p's codes ready; [9]: a
   // wait expired; [10 + p]: pair p's X has arrived
   __shared__ int sync_s[2 * kDecPairs + 2];
@@ -207,13 +213,14 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = wave & (kDecPairs - 1);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * NF;
   int8_t* xq_p = reinterpret_cast<int8_t*>(lds) + p * MR * XS;  // pair p's codes [MR][XS]
   short* list_s = reinterpret_cast<short*>(lds + kDecPairs * MR * XS);
   int8_t* sink = reinterpret_cast<int8_t*>(list_s + kDecPairs * WCOLS) + lane * 8;
-  // the epilogue's column constant of feature n0 + t % 16: loaded by the compute waves,
-  // and with fewer than 8 pairs by the stream waves too (the epilogue's threads, and its
-  // later outlier passes, then span both)
+  // the epilogue's column constant of feature n0 + t % 16 (two row groups: of feature
+  // n0 + t % 32, clamped to N - 1): loaded by the compute waves, and by the stream waves
+  // too with fewer than 8 pairs or two row groups (the epilogue's threads, or its later
+  // outlier passes, then span both)
   float aw_c = 0.0f;
 
   if (wave < kDecPairs) {
@@ -236,7 +243,10 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
         xv[m][j] = __builtin_bit_cast(
             v8h, buf_load16(xr, m < M ? static_cast<unsigned>(m * K + cc * 8) * 2u : kOOB));
     }
-    aw_c = a.a_w[n0 + (tid & 15)];
+    if constexpr (RG == 1)
+      aw_c = a.a_w[n0 + (tid & 15)];
+    else
+      aw_c = a.a_w[min(n0 + tid % NF, N - 1)];
     if (tid == 0)
 #pragma unroll
       for (int i = 0; i < 2 * kDecPairs + 2; ++i) sync_s[i] = 0;
@@ -324,6 +334,21 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
       const int k = 4 * i + (lane >> 4);
       const int col = k < ngather ? list_p[k] : 0;
       qv[i] = a.Wq[unit_offset(n0 + (lane & 15), col, ks)];
+    }
+    // second row group: the same columns for features n0 + 16 + l % 16 (clamped), and
+    // the column constants of both of this lane's staged features
+    int qv2[RG > 1 ? kStageLoads : 1];
+    float aw_st[2] = {0.0f, 0.0f};
+    if constexpr (RG > 1) {
+      const int nf = min(n0 + 16 + (lane & 15), N - 1);
+#pragma unroll
+      for (int i = 0; i < kStageLoads; ++i) {
+        const int k = 4 * i + (lane >> 4);
+        const int col = k < ngather ? list_p[k] : 0;
+        qv2[i] = a.Wq[unit_offset(nf, col, ks)];
+      }
+      aw_st[0] = a.a_w[n0 + (lane & 15)];
+      aw_st[1] = a.a_w[nf];
     }
     // (MR <= 2: the X values are copied from the registers below instead, a divergent
     // loop over the few lanes holding an outlier column; measured faster at one token,
@@ -425,9 +450,18 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kStageLoads; ++i) {
       const int k = 4 * i + (lane >> 4);
-      if (k < nstage)
-        wo_s[(first + k) * 16 + (lane & 15)] =
-            static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv[i]) * aw_c, 127.0f)));
+      if constexpr (RG == 1) {
+        if (k < nstage)
+          wo_s[(first + k) * 16 + (lane & 15)] =
+              static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv[i]) * aw_c, 127.0f)));
+      } else {
+        if (k < nstage) {
+          wo_s[(first + k) * NF + (lane & 15)] =
+              static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv[i]) * aw_st[0], 127.0f)));
+          wo_s[(first + k) * NF + 16 + (lane & 15)] =
+              static_cast<float>(static_cast<_Float16>(__fdiv_rn(static_cast<float>(qv2[i]) * aw_st[1], 127.0f)));
+        }
+      }
     }
     if constexpr (kXoGather) {
 #pragma unroll
@@ -461,23 +495,40 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
     for (int i = E; i < SPW; ++i)
       wf[i] = __builtin_nontemporal_load(
           reinterpret_cast<const v4i*>(wrow + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes));
+    // second row group (clamped to the last one of Wq past N: its products land in
+    // outputs that are not stored), all its units after the first group's
+    v4i wf2[RG > 1 ? SPW : 1];
+    if constexpr (RG > 1) {
+      const int8_t* wrow2 = a.Wq + static_cast<size_t>(min((n0 >> 4) + 1, (N >> 4) - 1)) * ks * kUnitBytes +
+                            (lane & 15) * kUnitK + 16 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < SPW; ++i)
+        wf2[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wrow2 + static_cast<size_t>(min(SPW * p + i, ks - 1)) * kUnitBytes));
+    }
     if constexpr (kDecPairs < 8) aw_c = a.a_w[n0 + (tid & 15)];
+    if constexpr (RG > 1) aw_c = a.a_w[min(n0 + tid % NF, N - 1)];
     if (!lds_wait_geq(&sync_s[1 + p], 1)) sync_s[kDecPairs + 1] = 1;
 
     // 9. int8 MFMA: D[feature][token] += Wq[n0 + feature, k] * Xq[token, k] over the
     // pair's steps; tokens past M multiply zeros
     const int tok = lane & 15, kg = lane >> 4;
-    v4i acc = v4i{};
+    v4i acc = v4i{}, acc2 = v4i{};
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const v4i t = *reinterpret_cast<const v4i*>(xq_p + min(tok, M - 1) * XS + 64 * i + 16 * kg);
       const v4i b = tok < M ? t : v4i{};
-      if (SPW * p + i < ks)  // wave-uniform
+      if (SPW * p + i < ks) {  // wave-uniform
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], b, acc, 0, 0, 0);
+        if constexpr (RG > 1) acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf2[i], b, acc2, 0, 0, 0);
+      }
     }
     // 16x16 accumulator layout: lane l, register r -> token l % 16, feature 4 (l / 16) + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[p][4 * kg + r][tok] = acc[r];
+    if constexpr (RG > 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[p][16 + 4 * kg + r][tok] = acc2[r];
   }
   lds_barrier();
 
@@ -490,64 +541,138 @@ __global__ __launch_bounds__(128 * P) void k_decode(DecodeArgs a) {
   for (int w = 0; w < kDecPairs; ++w) wb[w + 1] = wb[w] + cnt_s[w];
   const int count = wb[kDecPairs];
   const int npre = min(count, kPre);
-  const int m = tid >> 4, nl = tid & 15;
-  float yo = 0.0f;
-  if (tid < 256)
-    for (int r = 0; r < npre; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
-  for (int r0 = kPre; r0 < count; r0 += CO) {  // block-uniform trip count
-    lds_barrier();  // the staged values above are read
-    const int rn = min(CO, count - r0);
-    if (tid < CO * 16) {
-      const int pr = tid >> 4, pq = tid & 15;
-      int col = 0;
-      if (pr < rn) {
-        const int w = pair_of_rank<kDecPairs>(wb, r0 + pr);
-        col = list_s[w * WCOLS + r0 + pr - wb[w]];
-      }
-      const int q = a.Wq[unit_offset(n0 + pq, col, ks)];
-      const _Float16 x = a.X[static_cast<size_t>(min(pq, M - 1)) * K + col];
-      wo_s[pr * 16 + pq] = pr < rn ? static_cast<float>(static_cast<_Float16>(
-                                         __fdiv_rn(static_cast<float>(q) * aw_c, 127.0f)))
-                                   : 0.0f;
-      xo_s[pr * 16 + pq] = pr < rn && pq < M ? static_cast<float>(x) : 0.0f;
-    }
-    lds_barrier();
+  if constexpr (RG == 1) {
+    const int m = tid >> 4, nl = tid & 15;
+    float yo = 0.0f;
     if (tid < 256)
-      for (int r = 0; r < rn; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
-  }
-  const bool overflow = count > a.max_outliers;
-  const bool expired = sync_s[kDecPairs + 1] != 0;
-  if (tid < 256 && m < M) {
-    int s = 0;
+      for (int r = 0; r < npre; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
+    for (int r0 = kPre; r0 < count; r0 += CO) {  // block-uniform trip count
+      lds_barrier();  // the staged values above are read
+      const int rn = min(CO, count - r0);
+      if (tid < CO * 16) {
+        const int pr = tid >> 4, pq = tid & 15;
+        int col = 0;
+        if (pr < rn) {
+          const int w = pair_of_rank<kDecPairs>(wb, r0 + pr);
+          col = list_s[w * WCOLS + r0 + pr - wb[w]];
+        }
+        const int q = a.Wq[unit_offset(n0 + pq, col, ks)];
+        const _Float16 x = a.X[static_cast<size_t>(min(pq, M - 1)) * K + col];
+        wo_s[pr * 16 + pq] = pr < rn ? static_cast<float>(static_cast<_Float16>(
+                                           __fdiv_rn(static_cast<float>(q) * aw_c, 127.0f)))
+                                     : 0.0f;
+        xo_s[pr * 16 + pq] = pr < rn && pq < M ? static_cast<float>(x) : 0.0f;
+      }
+      lds_barrier();
+      if (tid < 256)
+        for (int r = 0; r < rn; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * 16 + nl], yo);
+    }
+    const bool overflow = count > a.max_outliers;
+    const bool expired = sync_s[kDecPairs + 1] != 0;
+    if (tid < 256 && m < M) {
+      int s = 0;
 #pragma unroll
-    for (int w = 0; w < kDecPairs; ++w) s += red[w][nl][m];
-    const float y = static_cast<float>(s) * (rowmax_s[m] * kInvQMax2) * aw_c + yo;
-    a.Y[static_cast<size_t>(m) * N + n0 + nl] =
-        overflow || expired ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y);
-    if (a.acc_out) a.acc_out[static_cast<size_t>(m) * N + n0 + nl] = s;
+      for (int w = 0; w < kDecPairs; ++w) s += red[w][nl][m];
+      const float y = static_cast<float>(s) * (rowmax_s[m] * kInvQMax2) * aw_c + yo;
+      a.Y[static_cast<size_t>(m) * N + n0 + nl] =
+          overflow || expired ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y);
+      if (a.acc_out) a.acc_out[static_cast<size_t>(m) * N + n0 + nl] = s;
+    }
+  } else {
+    // two row groups: thread t < 16 NF -> (token t / NF, feature n0 + t % NF); later
+    // passes stage weights by thread t < CO NF (rank t / NF, feature t % NF, that of its
+    // own column constant) and X by thread t < 16 CO (rank t / 16, token t % 16)
+    const int m = tid / NF, nl = tid % NF;
+    float yo = 0.0f;
+    if (tid < 16 * NF)
+      for (int r = 0; r < npre; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * NF + nl], yo);
+    auto col_of_rank = [&](int r) {
+      const int w = pair_of_rank<kDecPairs>(wb, r);
+      return static_cast<int>(list_s[w * WCOLS + r - wb[w]]);
+    };
+    for (int r0 = kPre; r0 < count; r0 += CO) {  // block-uniform trip count
+      lds_barrier();  // the staged values above are read
+      const int rn = min(CO, count - r0);
+      if (tid < CO * NF) {
+        const int pr = tid / NF;
+        const int col = pr < rn ? col_of_rank(r0 + pr) : 0;
+        const int q = a.Wq[unit_offset(min(n0 + nl, N - 1), col, ks)];
+        wo_s[pr * NF + nl] = pr < rn ? static_cast<float>(static_cast<_Float16>(
+                                           __fdiv_rn(static_cast<float>(q) * aw_c, 127.0f)))
+                                     : 0.0f;
+      }
+      if (tid < CO * 16) {
+        const int pr = tid >> 4, pq = tid & 15;
+        const int col = pr < rn ? col_of_rank(r0 + pr) : 0;
+        const _Float16 x = a.X[static_cast<size_t>(min(pq, M - 1)) * K + col];
+        xo_s[pr * 16 + pq] = pr < rn && pq < M ? static_cast<float>(x) : 0.0f;
+      }
+      lds_barrier();
+      if (tid < 16 * NF)
+        for (int r = 0; r < rn; ++r) yo = __builtin_fmaf(xo_s[r * 16 + m], wo_s[r * NF + nl], yo);
+    }
+    const bool overflow = count > a.max_outliers;
+    const bool expired = sync_s[kDecPairs + 1] != 0;
+    if (tid < 16 * NF && m < M && n0 + nl < N) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < kDecPairs; ++w) s += red[w][nl][m];
+      const float y = static_cast<float>(s) * (rowmax_s[m] * kInvQMax2) * aw_c + yo;
+      a.Y[static_cast<size_t>(m) * N + n0 + nl] =
+          overflow || expired ? static_cast<_Float16>(__builtin_nanf("")) : static_cast<_Float16>(y);
+      if (a.acc_out) a.acc_out[static_cast<size_t>(m) * N + n0 + nl] = s;
+    }
   }
   if (blockIdx.x == 0 && tid == 0) {
-    a.status[0] = overflow ? 7 : 0;
+    a.status[0] = count > a.max_outliers ? 7 : 0;
     a.status[1] = count;
   }
+}
+
+static int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      return 256;
+    cus = v;
+  }
+  return cus;
+}
+
+// Row groups per block: 2 where the 16-row groups of Wq outnumber the CUs (with one per
+// block the blocks would run in several rounds, each repeating the activation work), with
+// 8 pairs of waves, at most 8 K-steps per pair (the stream waves then hold 2 x 8 units)
+// and 8 token rows held. Measured per call: 8 x 4096 x 8192 14.0 -> 9.4 us, 8 x 4096 x
+// 16384 26.0 -> 16.9; with 1-4 rows, where the activation work is small, the doubled
+// weight stream per block lost (1 x 4096 x 12288 11.6 -> 14.3, 4 x 4096 x 11008 13.0 ->
+// 14.4), and 16 rows leave the compute waves no registers for it.
+static int decode_row_groups(int64_t M, int64_t K, int64_t N) {
+  return decode_pairs(M, K) == 8 && steps_per_wave(M, K) <= 8 && rows_held(M) == 8 &&
+                 N / 16 > device_cus()
+             ? 2
+             : 1;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const size_t lds = decode_lds_bytes(a.M, a.K);
   const int mr = rows_held(a.M), spw = steps_per_wave(a.M, a.K), pairs = decode_pairs(a.M, a.K);
-  const dim3 grid(a.N / 16), block(128 * pairs);
-#define I8MM_DEC(R, W, P)                                                \
-  if (mr == R && spw == W && pairs == P) {                               \
-    hipLaunchKernelGGL((k_decode<R, W, P>), grid, block, lds, s, a);     \
-    return hipGetLastError();                                            \
+  const int rg = decode_row_groups(a.M, a.K, a.N);
+  const dim3 grid((a.N / 16 + rg - 1) / rg), block(128 * pairs);
+#define I8MM_DEC(R, W, P, G)                                                     \
+  if (mr == R && spw == W && pairs == P && rg == G) {                            \
+    hipLaunchKernelGGL((k_decode<R, W, P, G>), grid, block, lds, s, a);          \
+    return hipGetLastError();                                                    \
   }
-  I8MM_DEC(1, 1, 8) I8MM_DEC(1, 2, 8) I8MM_DEC(1, 4, 8) I8MM_DEC(1, 8, 8) I8MM_DEC(1, 16, 8)
-  I8MM_DEC(2, 1, 8) I8MM_DEC(2, 2, 8) I8MM_DEC(2, 4, 8) I8MM_DEC(2, 8, 8) I8MM_DEC(2, 16, 8)
-  I8MM_DEC(4, 1, 8) I8MM_DEC(4, 2, 8) I8MM_DEC(4, 4, 8) I8MM_DEC(4, 8, 8) I8MM_DEC(4, 16, 8)
-  I8MM_DEC(8, 1, 8) I8MM_DEC(8, 2, 8) I8MM_DEC(8, 4, 8) I8MM_DEC(8, 8, 8) I8MM_DEC(8, 16, 8)
-  I8MM_DEC(16, 1, 8) I8MM_DEC(16, 2, 8) I8MM_DEC(16, 4, 8) I8MM_DEC(16, 8, 8)
-  I8MM_DEC(4, 8, 2) I8MM_DEC(8, 8, 2) I8MM_DEC(16, 8, 2)
-  I8MM_DEC(4, 8, 4) I8MM_DEC(8, 8, 4) I8MM_DEC(16, 8, 4)
+  I8MM_DEC(1, 1, 8, 1) I8MM_DEC(1, 2, 8, 1) I8MM_DEC(1, 4, 8, 1) I8MM_DEC(1, 8, 8, 1) I8MM_DEC(1, 16, 8, 1)
+  I8MM_DEC(2, 1, 8, 1) I8MM_DEC(2, 2, 8, 1) I8MM_DEC(2, 4, 8, 1) I8MM_DEC(2, 8, 8, 1) I8MM_DEC(2, 16, 8, 1)
+  I8MM_DEC(4, 1, 8, 1) I8MM_DEC(4, 2, 8, 1) I8MM_DEC(4, 4, 8, 1) I8MM_DEC(4, 8, 8, 1) I8MM_DEC(4, 16, 8, 1)
+  I8MM_DEC(8, 1, 8, 1) I8MM_DEC(8, 2, 8, 1) I8MM_DEC(8, 4, 8, 1) I8MM_DEC(8, 8, 8, 1) I8MM_DEC(8, 16, 8, 1)
+  I8MM_DEC(16, 1, 8, 1) I8MM_DEC(16, 2, 8, 1) I8MM_DEC(16, 4, 8, 1) I8MM_DEC(16, 8, 8, 1)
+  I8MM_DEC(4, 8, 2, 1) I8MM_DEC(8, 8, 2, 1) I8MM_DEC(16, 8, 2, 1)
+  I8MM_DEC(4, 8, 4, 1) I8MM_DEC(8, 8, 4, 1) I8MM_DEC(16, 8, 4, 1)
+  I8MM_DEC(8, 1, 8, 2) I8MM_DEC(8, 2, 8, 2) I8MM_DEC(8, 4, 8, 2) I8MM_DEC(8, 8, 8, 2)
 #undef I8MM_DEC
   return hipErrorInvalidValue;
 }

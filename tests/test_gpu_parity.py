@@ -264,6 +264,24 @@ def test_decode_many_outlier_columns(M, K):
     check_y(Y, ref["Y"])
 
 
+@pytest.mark.parametrize("M,K,N,dims", [(8, 4096, 4112, 4), (2, 2048, 8192, 4), (1, 512, 4128, 4),
+                                         (5, 2992, 4624, 4), (6, 2560, 8208, 40)])
+def test_decode_two_row_groups(M, K, N, dims):
+    """More 16-row groups of Wq than CUs: with 5-8 token rows each decode block takes two
+    row groups (32 output features) for one activation pass; odd counts leave the last
+    block one real row group (its second clamped, its outputs past N not stored); with 40
+    outlier columns the epilogue's later passes stage 32 features per rank. With one or
+    two rows the blocks keep one row group and run in several rounds."""
+    announce(f"decode two row groups M={M} K={K} N={N} dims={dims}")
+    assert binding.is_decode(M, K)
+    X = planted(7 * M + K + N, M, K, n_dims=dims, frac=1.0)
+    W = weight(K + N, K, N)
+    ref, Y, acc = _mixed(X, W, 6.0, mo=256)
+    assert ref["count"] == dims
+    assert np.array_equal(acc, ref["acc"])
+    check_y(Y, ref["Y"])
+
+
 @pytest.mark.parametrize("M,K,N", [(2048, 1024, 64), (600, 2000, 48)])
 def test_lone_outlier_rows_in_every_row_chunk(M, K, N):
     """Each outlier column holds one large value in a single row (first, middle and last
